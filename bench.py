@@ -1,0 +1,205 @@
+"""Benchmark of the MTP draft sweep on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config large]
+
+A step is one whole draft sweep (gather, both norms, concat, eh_proj, head norm,
+lm_head over the full vocabulary, argmax) for one batch of synthetic input
+already resident in HBM.  The default workload is the Large draft sweep
+(H = 6144, vocab = 154880, B = 1); `value` is BF16-head draft sweeps per second,
+and the FP8-head sweep is timed the same way and reported beside it.
+
+The roofline object covers the dominant kernel, the lm_head sweep: algorithmic
+bytes per launch (the weight matrix once, plus the per-row scales for FP8, the
+normed activation and the logits written) divided by the head call's average
+duration, timed with HIP events on the stream the kernels run on.  The
+cpu_baseline object times the FP64 oracle on a bounded sample of the same
+workload on the host cores.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "draft sweeps/sec and lm_head achieved HBM GB/s (% of peak), BF16 vs FP8"
+HBM_PEAK_GBPS = 8000.0
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=200)
+    p.add_argument("--warmup", type=int, default=20)
+    p.add_argument("--config", default="large", choices=["tiny", "mid", "large", "batched", "neartie"])
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-seconds", type=float, default=12.0,
+                   help="approximate budget for the oracle baseline sample")
+    return p.parse_args()
+
+
+def head_bytes(H: int, V: int, B: int, fp8: bool) -> int:
+    """Algorithmic bytes of one lm_head launch: every weight byte once (plus
+    one f32 scale per row for FP8), the x vectors and head-norm weight read,
+    and BF16 logits written."""
+    w = V * H * (1 if fp8 else 2) + (V * 4 if fp8 else 0)
+    return w + B * H * 2 + H * 2 + B * V * 2
+
+
+def sweep_bytes(H: int, V: int, B: int, fp8: bool) -> int:
+    """Algorithmic bytes of one whole sweep: eh_proj [H][2H] BF16, the head,
+    and per sequence the embedding row, the hidden row and the two norm weights."""
+    return 2 * H * H * 2 + head_bytes(H, V, B, fp8) + B * 2 * H * 2 + 2 * H * 2
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the sweep has no "
+              "multi-GPU path in this build.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import mtp_draft_head_embed_amd as mtp
+    import synth
+    from tests import harness
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    cfg = synth.CONFIGS[args.config]
+    H, V, B = cfg.hidden, cfg.vocab, cfg.batch
+    t0 = time.time()
+    wts = synth.make_weights(cfg)
+    tokens, hidden = synth.make_inputs(cfg)
+    print(f"[bench] {cfg.name}: weights generated in {time.time() - t0:.1f}s", file=sys.stderr,
+          flush=True)
+    dw = harness.upload(wts)
+    q, s = harness.quantize_dev(dw)
+    torch.cuda.synchronize()
+
+    tk = torch.from_numpy(tokens.astype(np.uint32).view(np.int32)).to(dev)
+    hd = harness.to_dev_bf16(hidden)
+    draft = torch.empty(B, dtype=torch.int32, device=dev)
+    logits = torch.empty((B, V), dtype=torch.bfloat16, device=dev)
+    ws = mtp.new_workspace(H, V, B)
+    x = torch.empty((B, H), dtype=torch.bfloat16, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def sweep(fp8):
+        if fp8:
+            mtp.mtp_draft_fp8w(dw.w, q, s, B, tk, hd, draft, logits, ws, stream)
+        else:
+            mtp.mtp_draft_bf16(dw.w, B, tk, hd, draft, logits, ws, stream)
+
+    def head(fp8):
+        if fp8:
+            mtp.mtp_head_fp8w(dw.w, q, s, B, x, draft, logits, ws, stream)
+        else:
+            mtp.mtp_head_bf16(dw.w, B, x, draft, logits, ws, stream)
+
+    def timed(fn, steps, warmup):
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        t_wall = time.perf_counter()
+        e0.record(stream)
+        for _ in range(steps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t_wall
+        return e0.elapsed_time(e1) / 1e3, wall
+
+    mtp.mtp_front(dw.w, B, tk, hd, x, ws, stream)
+    torch.cuda.synchronize()
+
+    res = {}
+    for name, fp8 in (("bf16", False), ("fp8", True)):
+        gpu_s, wall_s = timed(lambda: sweep(fp8), args.steps, args.warmup)
+        head_s, _ = timed(lambda: head(fp8), args.steps, args.warmup)
+        hb = head_bytes(H, V, B, fp8)
+        head_us = head_s / args.steps * 1e6
+        gbps = hb / (head_s / args.steps) / 1e9
+        res[name] = {
+            "sweeps_per_s": args.steps / wall_s,
+            "ms_per_step": wall_s / args.steps * 1e3,
+            "event_ms_per_step": gpu_s / args.steps * 1e3,
+            "head_us": head_us,
+            "lm_head_GBps": gbps,
+            "lm_head_frac_of_peak": gbps / HBM_PEAK_GBPS,
+            "sweep_GBps": sweep_bytes(H, V, B, fp8) / (gpu_s / args.steps) / 1e9,
+        }
+        print(f"[bench] {name}: {res[name]}", file=sys.stderr, flush=True)
+
+    main_path = "bf16"
+    r = res[main_path]
+    hb = head_bytes(H, V, B, False)
+    roof = {
+        "bound": "hbm",
+        "achieved": round(r["lm_head_GBps"], 1),
+        "peak": HBM_PEAK_GBPS,
+        "unit": "GB/s",
+        "frac": round(r["lm_head_GBps"] / HBM_PEAK_GBPS, 4),
+        "traffic": None,
+        "kernel": "row_gemv_kernel (lm_head, BF16) + argmax_final_kernel",
+        "algorithmic_bytes_per_launch": hb,
+        "avg_launch_us": round(r["head_us"], 2),
+    }
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+        nthreads = oracle.default_threads()
+        t_end = time.perf_counter() + args.cpu_seconds
+        n = 0
+        tc = time.perf_counter()
+        while True:
+            for b in range(B):
+                oracle.draft(wts, int(tokens[b]), hidden[b], nthreads=nthreads)
+            n += 1
+            if time.perf_counter() >= t_end:
+                break
+        el = time.perf_counter() - tc
+        cpu = {"value": round(n / el, 4), "unit": "draft sweeps/s", "cores": nthreads,
+               "kind": "oracle",
+               "sample": f"{n} full {cfg.name} BF16 draft sweep(s) (B={B}) through the FP64 "
+                         f"oracle, {el:.1f}s, {nthreads} threads splitting vocab rows"}
+
+    line = {
+        "metric": METRIC,
+        "value": round(r["sweeps_per_s"], 2),
+        "unit": "draft sweeps/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(r["ms_per_step"], 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"{cfg.name} draft sweep", "hidden": H, "vocab": V, "batch": B,
+                   "head": "bf16", "parallelism": "single GPU"},
+        "lm_head": {k: {"GBps": round(v["lm_head_GBps"], 1),
+                        "frac_of_peak": round(v["lm_head_frac_of_peak"], 4),
+                        "head_us": round(v["head_us"], 2),
+                        "sweeps_per_s": round(v["sweeps_per_s"], 2),
+                        "ms_per_step": round(v["ms_per_step"], 5)} for k, v in res.items()},
+        "roofline": roof,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

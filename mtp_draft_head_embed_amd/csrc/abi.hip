@@ -1,0 +1,257 @@
+// abi.hip -- the extern "C" entry points declared in include/mtp_draft.h.
+//
+// Host side only: argument validation (every host-visible error is returned
+// before anything is enqueued), workspace carving and kernel launches.  The
+// library keeps no state between calls.
+#include "../../include/mtp_draft.h"
+#include "common.hpp"
+#include "kernels.hpp"
+
+using namespace mtp;
+
+namespace {
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int check_shape(int32_t hidden, int32_t vocab, int32_t batch)
+{
+    if (hidden < 16 || hidden > MTP_MAX_HIDDEN || (hidden % 16) != 0)
+        return MTP_ERR_SHAPE;
+    if (vocab < 1 || vocab > MTP_MAX_VOCAB)
+        return MTP_ERR_SHAPE;
+    if (batch < 1 || batch > MTP_MAX_BATCH)
+        return MTP_ERR_SHAPE;
+    return MTP_OK;
+}
+
+// Every pointer in the list must be non-NULL and 16-byte aligned.
+int check_ptrs(std::initializer_list<const void *> ps)
+{
+    for (const void *p : ps)
+        if (!p)
+            return MTP_ERR_NULL;
+    for (const void *p : ps)
+        if (!aligned16(p))
+            return MTP_ERR_ALIGN;
+    return MTP_OK;
+}
+
+int check_opt_ptr(const void *p) { return (p && !aligned16(p)) ? MTP_ERR_ALIGN : MTP_OK; }
+
+int check_ws(const void *ws, size_t ws_bytes, int32_t hidden, int32_t batch)
+{
+    if (!ws)
+        return MTP_ERR_WORKSPACE;
+    if (!aligned16(ws))
+        return MTP_ERR_ALIGN;
+    if (ws_bytes < ws_layout(hidden, batch).total)
+        return MTP_ERR_WORKSPACE;
+    return MTP_OK;
+}
+
+#define MTP_TRY(expr)                 \
+    do {                              \
+        const int _rc = (expr);       \
+        if (_rc != MTP_OK)            \
+            return _rc;               \
+    } while (0)
+
+int validate_front(const mtp_weights *w, int32_t batch, const uint32_t *tokens, const void *hidden,
+                   const void *x)
+{
+    if (!w)
+        return MTP_ERR_NULL;
+    MTP_TRY(check_shape(w->hidden, w->vocab, batch));
+    MTP_TRY(check_ptrs({w->embed, w->enorm_w, w->hnorm_w, w->eh_proj, tokens, hidden, x}));
+    return MTP_OK;
+}
+
+int validate_head(const mtp_weights *w, bool fp8, const uint8_t *q, const float *scale,
+                  int32_t batch, const void *x, const uint32_t *draft, const void *logits)
+{
+    if (!w)
+        return MTP_ERR_NULL;
+    MTP_TRY(check_shape(w->hidden, w->vocab, batch));
+    if (fp8)
+        MTP_TRY(check_ptrs({w->head_norm_w, q, scale, x, draft}));
+    else
+        MTP_TRY(check_ptrs({w->head_norm_w, w->lm_head, x, draft}));
+    MTP_TRY(check_opt_ptr(logits));
+    return MTP_OK;
+}
+
+int validate_draft(const mtp_weights *w, bool fp8, const uint8_t *q, const float *scale,
+                   int32_t batch, const uint32_t *tokens, const void *hidden, const uint32_t *draft,
+                   const void *logits, const void *ws, size_t ws_bytes)
+{
+    if (!w)
+        return MTP_ERR_NULL;
+    MTP_TRY(check_shape(w->hidden, w->vocab, batch));
+    MTP_TRY(check_ptrs({w->embed, w->enorm_w, w->hnorm_w, w->eh_proj, w->head_norm_w, tokens,
+                        hidden, draft}));
+    if (fp8)
+        MTP_TRY(check_ptrs({q, scale}));
+    else
+        MTP_TRY(check_ptrs({w->lm_head}));
+    MTP_TRY(check_opt_ptr(logits));
+    MTP_TRY(check_ws(ws, ws_bytes, w->hidden, batch));
+    return MTP_OK;
+}
+
+RowGemvArgs front_args(const mtp_weights *w, const uint32_t *tokens, const void *hidden, void *x)
+{
+    RowGemvArgs a{};
+    a.W = w->eh_proj;
+    a.N = w->hidden;
+    a.K = 2 * w->hidden;
+    a.embed = static_cast<const uint16_t *>(w->embed);
+    a.vocab = w->vocab;
+    a.tokens = tokens;
+    a.hidden = static_cast<const uint16_t *>(hidden);
+    a.enorm_w = static_cast<const uint16_t *>(w->enorm_w);
+    a.hnorm_w = static_cast<const uint16_t *>(w->hnorm_w);
+    a.eps = w->rms_eps;
+    a.out = static_cast<uint16_t *>(x);
+    return a;
+}
+
+int run_head(const mtp_weights *w, bool fp8, const uint8_t *q, const float *scale, int32_t batch,
+             const void *x, const uint32_t *tokens, uint32_t *draft, void *logits, void *ws,
+             hipStream_t s)
+{
+    const WsLayout L = ws_layout(w->hidden, batch);
+    Partial *parts = reinterpret_cast<Partial *>(static_cast<char *>(ws) + L.part_off);
+    RowGemvArgs a{};
+    a.W = fp8 ? static_cast<const void *>(q) : w->lm_head;
+    a.scale = scale;
+    a.N = w->vocab;
+    a.K = w->hidden;
+    a.xin = static_cast<const uint16_t *>(x);
+    a.norm_w = static_cast<const uint16_t *>(w->head_norm_w);
+    a.eps = w->rms_eps;
+    a.logits = static_cast<uint16_t *>(logits);
+    a.partials = parts;
+    const int grid = head_grid(w->vocab, device_cu_count());
+    if (launch_head(a, fp8, grid, batch, s) != hipSuccess)
+        return MTP_ERR_HIP;
+    if (launch_argmax_final(parts, grid, tokens, w->vocab, draft, batch, s) != hipSuccess)
+        return MTP_ERR_HIP;
+    return MTP_OK;
+}
+
+int run_draft(const mtp_weights *w, bool fp8, const uint8_t *q, const float *scale,
+              int32_t batch, const uint32_t *tokens, const void *hidden, uint32_t *draft,
+              void *logits, void *ws, size_t ws_bytes, void *stream)
+{
+    MTP_TRY(validate_draft(w, fp8, q, scale, batch, tokens, hidden, draft, logits, ws, ws_bytes));
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const WsLayout L = ws_layout(w->hidden, batch);
+    void *x = static_cast<char *>(ws) + L.x_off;
+    if (launch_eh_proj(front_args(w, tokens, hidden, x), batch, s) != hipSuccess)
+        return MTP_ERR_HIP;
+    return run_head(w, fp8, q, scale, batch, x, tokens, draft, logits, ws, s);
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t mtp_workspace_bytes(int32_t hidden, int32_t vocab, int32_t batch)
+{
+    if (check_shape(hidden, vocab, batch) != MTP_OK)
+        return 0;
+    return ws_layout(hidden, batch).total;
+}
+
+int mtp_validate_draft_args(const mtp_weights *w, int fp8, const uint8_t *q, const float *scale,
+                            int32_t batch, const uint32_t *tokens, const void *hidden,
+                            const uint32_t *draft, const void *logits, const void *workspace,
+                            size_t ws_bytes)
+{
+    return validate_draft(w, fp8 != 0, q, scale, batch, tokens, hidden, draft, logits, workspace,
+                          ws_bytes);
+}
+
+int mtp_quantize_head_fp8(const void *lm_head_bf16, int32_t vocab, int32_t hidden, uint8_t *q,
+                          float *scale, void *workspace, size_t ws_bytes, void *stream)
+{
+    MTP_TRY(check_shape(hidden, vocab, 1));
+    MTP_TRY(check_ptrs({lm_head_bf16, q, scale}));
+    if (!workspace || ws_bytes < 256)
+        return MTP_ERR_WORKSPACE;
+    if (!aligned16(workspace))
+        return MTP_ERR_ALIGN;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    uint32_t *flag = static_cast<uint32_t *>(workspace);
+    if (launch_quantize(static_cast<const uint16_t *>(lm_head_bf16), vocab, hidden, q, scale, flag,
+                        s) != hipSuccess)
+        return MTP_ERR_HIP;
+    uint32_t h_flag = 0;
+    if (hipMemcpyAsync(&h_flag, flag, sizeof h_flag, hipMemcpyDeviceToHost, s) != hipSuccess)
+        return MTP_ERR_HIP;
+    if (hipStreamSynchronize(s) != hipSuccess)
+        return MTP_ERR_HIP;
+    return h_flag ? MTP_ERR_NONFINITE : MTP_OK;
+}
+
+int mtp_draft_bf16(const mtp_weights *w, int32_t batch, const uint32_t *tokens,
+                   const void *hidden, uint32_t *draft, void *logits, void *workspace,
+                   size_t ws_bytes, void *stream)
+{
+    return run_draft(w, false, nullptr, nullptr, batch, tokens, hidden, draft, logits, workspace,
+                     ws_bytes, stream);
+}
+
+int mtp_draft_fp8w(const mtp_weights *w, const uint8_t *q, const float *scale, int32_t batch,
+                   const uint32_t *tokens, const void *hidden, uint32_t *draft, void *logits,
+                   void *workspace, size_t ws_bytes, void *stream)
+{
+    return run_draft(w, true, q, scale, batch, tokens, hidden, draft, logits, workspace, ws_bytes,
+                     stream);
+}
+
+int mtp_front(const mtp_weights *w, int32_t batch, const uint32_t *tokens, const void *hidden,
+              void *x, void *workspace, size_t ws_bytes, void *stream)
+{
+    MTP_TRY(validate_front(w, batch, tokens, hidden, x));
+    MTP_TRY(check_ws(workspace, ws_bytes, w->hidden, batch));
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (launch_eh_proj(front_args(w, tokens, hidden, x), batch, s) != hipSuccess)
+        return MTP_ERR_HIP;
+    return MTP_OK;
+}
+
+int mtp_head_bf16(const mtp_weights *w, int32_t batch, const void *x, uint32_t *draft,
+                  void *logits, void *workspace, size_t ws_bytes, void *stream)
+{
+    MTP_TRY(validate_head(w, false, nullptr, nullptr, batch, x, draft, logits));
+    MTP_TRY(check_ws(workspace, ws_bytes, w->hidden, batch));
+    return run_head(w, false, nullptr, nullptr, batch, x, nullptr, draft, logits, workspace,
+                    static_cast<hipStream_t>(stream));
+}
+
+int mtp_head_fp8w(const mtp_weights *w, const uint8_t *q, const float *scale, int32_t batch,
+                  const void *x, uint32_t *draft, void *logits, void *workspace,
+                  size_t ws_bytes, void *stream)
+{
+    MTP_TRY(validate_head(w, true, q, scale, batch, x, draft, logits));
+    MTP_TRY(check_ws(workspace, ws_bytes, w->hidden, batch));
+    return run_head(w, true, q, scale, batch, x, nullptr, draft, logits, workspace,
+                    static_cast<hipStream_t>(stream));
+}
+
+const char *mtp_status_str(int status)
+{
+    switch (status) {
+    case MTP_OK: return "ok";
+    case MTP_ERR_NULL: return "a required pointer is NULL";
+    case MTP_ERR_SHAPE: return "hidden, vocab or batch out of range";
+    case MTP_ERR_ALIGN: return "a device pointer is not 16-byte aligned";
+    case MTP_ERR_WORKSPACE: return "workspace missing or too small";
+    case MTP_ERR_NONFINITE: return "a weight is NaN or Inf";
+    case MTP_ERR_HIP: return "HIP runtime error";
+    default: return "unknown status";
+    }
+}
+
+}  // extern "C"

@@ -1,0 +1,349 @@
+// row_gemv.hip -- bandwidth-bound GEMV over row-major weights, one wavefront
+// per output row, for the single-sequence draft sweep on gfx950.
+//
+// Covers three steps of `forward_one` (metrale_model_arch/glm5next_mtp_head.rs):
+//   * eh_proj:  x = BF16(eh_proj . [enorm(embed[token]) | hnorm(hidden)]).
+//     The gather and both vanilla norms run as this kernel's prologue (each
+//     workgroup rebuilds the [2H] concat in LDS), so no separate norm launches.
+//   * lm_head, BF16 (`dense_gemv`) and FP8 (`dense_gemv_fp8w`): the
+//     `shared_head.norm` of x runs as the prologue (the normed BF16 vector is
+//     staged in LDS) and the argmax runs as the epilogue: every logit is rounded
+//     to BF16, optionally stored, and each workgroup leaves its best (value,
+//     index) in a partials array that argmax_final reduces.
+//
+// Memory pattern: lane l of a wave reads 16 contiguous bytes at column
+// c*CW + l*EPL of its row (CW = 64 lanes x EPL elements), so each load
+// instruction of a wave fetches 1 KiB of one row; RPI rows x U chunks are in
+// flight per wave.  Rows are dealt to the waves of the whole grid round-robin,
+// so at any moment the grid streams one contiguous window of the matrix.  The
+// activation vector is read from LDS (BF16), once per 16-byte weight chunk.
+//
+// Sums are FP32 in a fixed order (per lane over its chunks, then a fixed xor
+// butterfly), so results do not depend on grid size or timing.
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace mtp {
+
+// Sum of squares of a BF16 vector of n elements (n % 8 == 0, n <= 8192),
+// reduced over the whole workgroup in a fixed order.  `v` receives the
+// thread's 16-byte pieces (element (i*blockDim + tid)*8) for reuse.
+__device__ __forceinline__ float block_sumsq(const uint16_t *__restrict__ src, int n, bool valid,
+                                             uint4 (&v)[4], float *red)
+{
+    const int tid = threadIdx.x;
+    float ss = 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int j = (i * blockDim.x + tid) * 8;
+        v[i] = make_uint4(0, 0, 0, 0);
+        if (valid && j < n)
+            v[i] = *reinterpret_cast<const uint4 *>(src + j);
+        const uint32_t w[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const float a = bf16_lo(w[q]), b = bf16_hi(w[q]);
+            ss = fmaf(a, a, ss);
+            ss = fmaf(b, b, ss);
+        }
+    }
+    ss = wave_sum(ss);
+    const int nw = blockDim.x / kWave;
+    __syncthreads();
+    if ((tid & (kWave - 1)) == 0)
+        red[tid / kWave] = ss;
+    __syncthreads();
+    float tot = 0.f;
+    for (int w = 0; w < nw; ++w)
+        tot += red[w];
+    return tot;
+}
+
+// out[j] = BF16(x_j * w_j / r) for the thread's pieces, written to LDS.
+__device__ __forceinline__ void norm_to_lds(const uint4 (&v)[4], const uint16_t *__restrict__ w,
+                                            int n, float r, uint16_t *dst)
+{
+    const int tid = threadIdx.x;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int j = (i * blockDim.x + tid) * 8;
+        if (j < n) {
+            const uint4 wv = *reinterpret_cast<const uint4 *>(w + j);
+            const uint32_t xa[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
+            const uint32_t wa[4] = {wv.x, wv.y, wv.z, wv.w};
+            uint32_t o[4];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const float lo = (bf16_lo(xa[q]) * bf16_lo(wa[q])) / r;
+                const float hi = (bf16_hi(xa[q]) * bf16_hi(wa[q])) / r;
+                o[q] = pack_bf16x2(lo, hi);
+            }
+            *reinterpret_cast<uint4 *>(dst + j) = make_uint4(o[0], o[1], o[2], o[3]);
+        }
+    }
+}
+
+// Dot of 8 BF16 weights with 8 BF16 activations, accumulated in order.
+__device__ __forceinline__ float dot8_bf16(const uint4 &w, const uint4 &a, float acc)
+{
+    acc = fmaf(bf16_lo(w.x), bf16_lo(a.x), acc);
+    acc = fmaf(bf16_hi(w.x), bf16_hi(a.x), acc);
+    acc = fmaf(bf16_lo(w.y), bf16_lo(a.y), acc);
+    acc = fmaf(bf16_hi(w.y), bf16_hi(a.y), acc);
+    acc = fmaf(bf16_lo(w.z), bf16_lo(a.z), acc);
+    acc = fmaf(bf16_hi(w.z), bf16_hi(a.z), acc);
+    acc = fmaf(bf16_lo(w.w), bf16_lo(a.w), acc);
+    acc = fmaf(bf16_hi(w.w), bf16_hi(a.w), acc);
+    return acc;
+}
+
+// Dot of 4 E4M3FN codes (one dword) with 4 BF16 activations (two dwords).
+// gfx950's v_cvt_pk_f32_fp8 decodes OCP E4M3FN exactly.
+__device__ __forceinline__ float dot4_fp8(uint32_t q, uint32_t a01, uint32_t a23, float acc)
+{
+    typedef float f2 __attribute__((ext_vector_type(2)));
+    const f2 d01 = __builtin_amdgcn_cvt_pk_f32_fp8(int(q), false);
+    const f2 d23 = __builtin_amdgcn_cvt_pk_f32_fp8(int(q), true);
+    acc = fmaf(d01.x, bf16_lo(a01), acc);
+    acc = fmaf(d01.y, bf16_hi(a01), acc);
+    acc = fmaf(d23.x, bf16_lo(a23), acc);
+    acc = fmaf(d23.y, bf16_hi(a23), acc);
+    return acc;
+}
+
+template <bool FP8, int PRO, int EPI, int RPI, int U>
+__global__ __launch_bounds__(256) void row_gemv_kernel(RowGemvArgs a)
+{
+    extern __shared__ uint4 lds_raw[];
+    __shared__ float red[16];
+    __shared__ float best_v_s[16];
+    __shared__ uint32_t best_i_s[16];
+    uint16_t *act = reinterpret_cast<uint16_t *>(lds_raw);
+
+    const int b = blockIdx.y;
+    const int tid = threadIdx.x;
+    const int lane = tid & (kWave - 1);
+    const int wid = tid / kWave;
+    const int K = a.K;
+
+    // ---- prologue: the BF16 activation vector act[0..K) in LDS -------------
+    if (PRO == PRO_FRONT) {
+        // K = 2H: [enorm(embed[token]) | hnorm(hidden[b])]
+        const int H = K / 2;
+        const uint32_t tok = a.tokens[b];
+        const bool tok_ok = tok < uint32_t(a.vocab);
+        const uint16_t *erow = a.embed + (tok_ok ? size_t(tok) * size_t(H) : 0);
+        uint4 v[4];
+        float ss = block_sumsq(erow, H, tok_ok, v, red);
+        norm_to_lds(v, a.enorm_w, H, sqrtf(ss / float(H) + a.eps), act);
+        ss = block_sumsq(a.hidden + size_t(b) * H, H, true, v, red);
+        norm_to_lds(v, a.hnorm_w, H, sqrtf(ss / float(H) + a.eps), act + H);
+    } else {
+        // K = H: shared_head.norm(x[b])
+        uint4 v[4];
+        const float ss = block_sumsq(a.xin + size_t(b) * K, K, true, v, red);
+        norm_to_lds(v, a.norm_w, K, sqrtf(ss / float(K) + a.eps), act);
+    }
+    __syncthreads();
+
+    // ---- row sweep ---------------------------------------------------------
+    constexpr int EPL = FP8 ? 16 : 8;       // elements per 16-byte load
+    constexpr int CW = kWave * EPL;         // columns per wave-wide load
+    constexpr int ESZ = FP8 ? 1 : 2;        // bytes per weight element
+    const int nchunks = (K + CW - 1) / CW;
+    const int wpb = blockDim.x / kWave;
+    const int Wt = gridDim.x * wpb;
+    const int gw = blockIdx.x * wpb + wid;
+    const int N = a.N;
+    const char *Wb = reinterpret_cast<const char *>(a.W);
+
+    float best_v = -INFINITY;
+    uint32_t best_i = 0xFFFFFFFFu;
+
+    for (int r0 = gw; r0 < N; r0 += Wt * RPI) {
+        float acc[RPI];
+#pragma unroll
+        for (int k = 0; k < RPI; ++k)
+            acc[k] = 0.f;
+        for (int c0 = 0; c0 < nchunks; c0 += U) {
+            uint4 wv[RPI][U];
+#pragma unroll
+            for (int k = 0; k < RPI; ++k) {
+                const int r = r0 + k * Wt;
+#pragma unroll
+                for (int u = 0; u < U; ++u) {
+                    const int col = (c0 + u) * CW + lane * EPL;
+                    wv[k][u] = make_uint4(0, 0, 0, 0);
+                    if (r < N && col < K)
+                        wv[k][u] = *reinterpret_cast<const uint4 *>(
+                            Wb + (size_t(r) * size_t(K) + size_t(col)) * ESZ);
+                }
+            }
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int col = (c0 + u) * CW + lane * EPL;
+                if (col < K) {
+                    if (!FP8) {
+                        const uint4 av = *reinterpret_cast<const uint4 *>(act + col);
+#pragma unroll
+                        for (int k = 0; k < RPI; ++k)
+                            acc[k] = dot8_bf16(wv[k][u], av, acc[k]);
+                    } else {
+                        const uint4 a0 = *reinterpret_cast<const uint4 *>(act + col);
+                        const uint4 a1 = *reinterpret_cast<const uint4 *>(act + col + 8);
+#pragma unroll
+                        for (int k = 0; k < RPI; ++k) {
+                            float s = acc[k];
+                            s = dot4_fp8(wv[k][u].x, a0.x, a0.y, s);
+                            s = dot4_fp8(wv[k][u].y, a0.z, a0.w, s);
+                            s = dot4_fp8(wv[k][u].z, a1.x, a1.y, s);
+                            s = dot4_fp8(wv[k][u].w, a1.z, a1.w, s);
+                            acc[k] = s;
+                        }
+                    }
+                }
+            }
+        }
+#pragma unroll
+        for (int k = 0; k < RPI; ++k) {
+            const int r = r0 + k * Wt;
+            const float sum = wave_sum(acc[k]);
+            if (r < N) {
+                if (EPI == EPI_STORE) {
+                    if (lane == 0)
+                        a.out[size_t(b) * N + r] = uint16_t(f32_to_bf16_bits(sum));
+                } else {
+                    const float z = FP8 ? sum * a.scale[r] : sum;
+                    const uint32_t lb = f32_to_bf16_bits(z);
+                    if (lane == 0 && a.logits)
+                        a.logits[size_t(b) * N + r] = uint16_t(lb);
+                    const float lv = __uint_as_float(lb << 16);
+                    if (better(lv, uint32_t(r), best_v, best_i)) {
+                        best_v = lv;
+                        best_i = uint32_t(r);
+                    }
+                }
+            }
+        }
+    }
+
+    if (EPI == EPI_ARGMAX) {
+        // every lane holds the same best (the sums were all-reduced)
+        if (lane == 0) {
+            best_v_s[wid] = best_v;
+            best_i_s[wid] = best_i;
+        }
+        __syncthreads();
+        if (tid == 0) {
+            float bv = best_v_s[0];
+            uint32_t bi = best_i_s[0];
+            for (int w = 1; w < wpb; ++w)
+                if (better(best_v_s[w], best_i_s[w], bv, bi)) {
+                    bv = best_v_s[w];
+                    bi = best_i_s[w];
+                }
+            a.partials[size_t(b) * kMaxHeadBlocks + blockIdx.x] = Partial{bv, bi};
+        }
+    }
+}
+
+// Second argmax stage: one workgroup per sequence reduces its partials.
+__global__ __launch_bounds__(256) void argmax_final_kernel(const Partial *__restrict__ partials,
+                                                           int nparts, const uint32_t *tokens,
+                                                           int vocab, uint32_t *draft)
+{
+    __shared__ float sv[4];
+    __shared__ uint32_t si[4];
+    const int b = blockIdx.x;
+    const int tid = threadIdx.x;
+    float bv = -INFINITY;
+    uint32_t bi = 0xFFFFFFFFu;
+    for (int p = tid; p < nparts; p += blockDim.x) {
+        const Partial q = partials[size_t(b) * kMaxHeadBlocks + p];
+        if (better(q.val, q.idx, bv, bi)) {
+            bv = q.val;
+            bi = q.idx;
+        }
+    }
+    wave_argmax(bv, bi);
+    if ((tid & (kWave - 1)) == 0) {
+        sv[tid / kWave] = bv;
+        si[tid / kWave] = bi;
+    }
+    __syncthreads();
+    if (tid == 0) {
+        for (int w = 1; w < int(blockDim.x / kWave); ++w)
+            if (better(sv[w], si[w], bv, bi)) {
+                bv = sv[w];
+                bi = si[w];
+            }
+        // wave 0's value is in bv already (lane 0 of wave 0 is tid 0)
+        if (tokens && tokens[b] >= uint32_t(vocab))
+            bi = 0xFFFFFFFFu;
+        draft[b] = bi;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Host launchers
+// ---------------------------------------------------------------------------
+
+template <bool FP8, int PRO, int EPI, int RPI, int U>
+static hipError_t launch_one(const RowGemvArgs &a, int grid, int batch, hipStream_t s)
+{
+    const size_t lds = align256(size_t(a.K) * 2);
+    hipLaunchKernelGGL((row_gemv_kernel<FP8, PRO, EPI, RPI, U>), dim3(grid, batch), dim3(256),
+                       lds, s, a);
+    return hipGetLastError();
+}
+
+int device_cu_count()
+{
+    int dev = 0, n = 0;
+    if (hipGetDevice(&dev) != hipSuccess)
+        return 256;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+        return 256;
+    return n;
+}
+
+hipError_t launch_eh_proj(const RowGemvArgs &a, int batch, hipStream_t s)
+{
+    // RPI = 2 rows per wave pass, 4 waves per workgroup: one pass over N rows
+    // needs N / 8 workgroups; a few passes per wave keep the grid resident.
+    const int waves = (a.N + 1) / 2;
+    int grid = (waves + 3) / 4;
+    if (grid > kMaxHeadBlocks)
+        grid = kMaxHeadBlocks;
+    return launch_one<false, PRO_FRONT, EPI_STORE, 2, 8>(a, grid, batch, s);
+}
+
+int head_grid(int N, int cu_count)
+{
+    int grid = cu_count * 4;
+    const int need = (N + 7) / 8;
+    if (grid > need)
+        grid = need;
+    if (grid > kMaxHeadBlocks)
+        grid = kMaxHeadBlocks;
+    if (grid < 1)
+        grid = 1;
+    return grid;
+}
+
+hipError_t launch_head(const RowGemvArgs &a, bool fp8, int grid, int batch, hipStream_t s)
+{
+    if (fp8)
+        return launch_one<true, PRO_HEADNORM, EPI_ARGMAX, 4, 4>(a, grid, batch, s);
+    return launch_one<false, PRO_HEADNORM, EPI_ARGMAX, 2, 8>(a, grid, batch, s);
+}
+
+hipError_t launch_argmax_final(const Partial *partials, int nparts, const uint32_t *tokens,
+                               int vocab, uint32_t *draft, int batch, hipStream_t s)
+{
+    hipLaunchKernelGGL(argmax_final_kernel, dim3(batch), dim3(256), 0, s, partials, nparts,
+                       tokens, vocab, draft);
+    return hipGetLastError();
+}
+
+}  // namespace mtp

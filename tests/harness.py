@@ -1,0 +1,143 @@
+"""GPU-side helpers for the parity tests, the smoke check and the benchmark.
+
+Uploads synthetic BF16 weights, runs the library through its Python binding,
+and applies the comparison rules of the draft sweep:
+
+  * FP8 codes and scales: bit-exact.
+  * logits: max_v |g_v - o_v| <= tol_b, where g is the GPU's BF16 logit, o the
+    oracle's unrounded FP64 logit and tol_b = 2e-2 * sigma_b (BF16 head) or
+    6e-2 * sigma_b (FP8 head, against the FP8 oracle on the same bytes), sigma_b
+    the population std of the oracle logits of sequence b.  When the BF16
+    half-ulp at the largest |o| exceeds tol_b, BF16 storage alone could break
+    the bound; the gate then widens to that half-ulp (and says so).
+  * draft: equal to the oracle's whenever the oracle's top-1 / top-2 gap
+    exceeds 2 tol_b; always equal to the lowest index of the GPU's own largest
+    returned logit; always inside the oracle's near-max set {o_v >= o_max - 2 tol}.
+"""
+from __future__ import annotations
+
+import dataclasses
+
+import numpy as np
+import torch
+
+import mtp_draft_head_embed_amd as mtp
+
+TOL_BF16 = 2e-2
+TOL_FP8 = 6e-2
+
+
+def to_dev_bf16(a: np.ndarray, device="cuda") -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(device).view(torch.bfloat16)
+
+
+def bf16_bits(t: torch.Tensor) -> np.ndarray:
+    return t.detach().view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def bf16_order_key(b: np.ndarray) -> np.ndarray:
+    """Integer key, monotone in the BF16 value, with +0 and -0 both 0; key
+    differences count BF16 ulps."""
+    b = np.asarray(b, dtype=np.uint16).astype(np.int64)
+    mag = b & 0x7FFF
+    return np.where(b & 0x8000, -mag, mag)
+
+
+def bits_to_f64(b: np.ndarray) -> np.ndarray:
+    return (np.asarray(b, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+@dataclasses.dataclass
+class DevWeights:
+    w: mtp.mtp_weights
+    tensors: dict
+    hidden: int
+    vocab: int
+
+
+def upload(weights: dict, device="cuda", with_lm_head=True) -> DevWeights:
+    t = {k: to_dev_bf16(weights[k], device) for k in
+         ("embed", "enorm_w", "hnorm_w", "head_norm_w", "eh_proj")}
+    t["lm_head"] = to_dev_bf16(weights["lm_head"], device) if with_lm_head else None
+    w = mtp.mtp_weights(t["embed"], t["enorm_w"], t["hnorm_w"], t["head_norm_w"], t["eh_proj"],
+                        t["lm_head"], weights["rms_eps"])
+    V, H = weights["embed"].shape
+    return DevWeights(w, t, H, V)
+
+
+def quantize_dev(dw: DevWeights, device="cuda"):
+    V, H = dw.vocab, dw.hidden
+    q = torch.empty((V, H), dtype=torch.uint8, device=device)
+    s = torch.empty(V, dtype=torch.float32, device=device)
+    ws = torch.empty(256, dtype=torch.uint8, device=device)
+    mtp.mtp_quantize_head_fp8(dw.tensors["lm_head"], V, H, q, s, ws)
+    return q, s
+
+
+def run_draft(dw: DevWeights, tokens: np.ndarray, hidden: np.ndarray, fp8=None,
+              with_logits=True, device="cuda"):
+    """Returns (draft uint32 [B], logits BF16 bits [B][V] or None)."""
+    B = int(tokens.size)
+    tk = torch.from_numpy(tokens.astype(np.uint32).view(np.int32)).to(device)
+    hd = to_dev_bf16(hidden.reshape(B, dw.hidden), device)
+    dr = torch.empty(B, dtype=torch.int32, device=device)
+    lg = torch.empty((B, dw.vocab), dtype=torch.bfloat16, device=device) if with_logits else None
+    ws = mtp.new_workspace(dw.hidden, dw.vocab, B, device)
+    if fp8 is None:
+        mtp.mtp_draft_bf16(dw.w, B, tk, hd, dr, lg, ws)
+    else:
+        mtp.mtp_draft_fp8w(dw.w, fp8[0], fp8[1], B, tk, hd, dr, lg, ws)
+    torch.cuda.synchronize()
+    d = dr.cpu().numpy().view(np.uint32)
+    return d, (bf16_bits(lg) if lg is not None else None)
+
+
+@dataclasses.dataclass
+class SeqReport:
+    b: int
+    sigma: float
+    tol: float
+    gate: float
+    widened: bool
+    max_err: float
+    gap: float
+    draft_gpu: int
+    draft_oracle: int
+    gated_exact: bool
+    ok: bool
+    why: str
+
+
+def compare_sequence(b: int, o: np.ndarray, g_bits: np.ndarray | None, draft_gpu: int,
+                     draft_oracle: int, tol_rel: float) -> SeqReport:
+    """Apply the comparison rules to one sequence."""
+    sigma = float(np.std(o))
+    tol = tol_rel * sigma
+    omax = float(np.max(np.abs(o)))
+    # half-ulp of BF16 at the largest logit magnitude
+    e = int(np.floor(np.log2(omax))) if omax > 0 else -126
+    half_ulp = 2.0 ** (e - 8)
+    gate = max(tol, half_ulp + 1e-6 * max(omax, 1.0))
+    widened = gate > tol
+    order = np.argsort(-o, kind="stable")
+    top1 = float(o[order[0]])
+    top2 = float(o[order[1]]) if o.size > 1 else -np.inf
+    gap = top1 - top2
+    why = []
+    max_err = float("nan")
+    if g_bits is not None:
+        g = bits_to_f64(g_bits)
+        max_err = float(np.max(np.abs(g - o)))
+        if not max_err <= gate:
+            why.append(f"logit error {max_err:.4g} > gate {gate:.4g}")
+        m = g.max()
+        own = int(np.nonzero(g == m)[0][0])
+        if draft_gpu != own:
+            why.append(f"draft {draft_gpu} is not the lowest argmax {own} of the returned logits")
+    gated = gap > 2 * gate
+    if gated and draft_gpu != draft_oracle:
+        why.append(f"gap {gap:.4g} > 2 gate but draft {draft_gpu} != oracle {draft_oracle}")
+    if not (0 <= draft_gpu < o.size) or o[draft_gpu] < top1 - 2 * gate:
+        why.append(f"draft {draft_gpu} outside the near-max set")
+    return SeqReport(b, sigma, tol, gate, widened, max_err, gap, int(draft_gpu), int(draft_oracle),
+                     gated, not why, "; ".join(why))

@@ -1,0 +1,117 @@
+"""Host-only checks of the C ABI (no GPU): the library loads, exports every
+entry point include/mtp_draft.h declares, and its host-side validation returns
+the documented status codes before anything would be enqueued."""
+import ctypes
+import os
+import re
+
+import pytest
+import torch
+
+import mtp_draft_head_embed_amd as mtp
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mtp_draft.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(mtp_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_symbols_exported():
+    names = declared_functions()
+    assert len(names) >= 9, names
+    L = mtp.lib()
+    for n in names:
+        assert hasattr(L, n), n
+        # and the Python binding carries the same name
+        assert hasattr(mtp, n), n
+
+
+def test_status_strings():
+    for code in range(7):
+        assert mtp.mtp_status_str(code)
+    assert mtp.mtp_status_str(99) == "unknown status"
+
+
+def test_workspace_bytes():
+    assert mtp.mtp_workspace_bytes(6144, 154880, 1) > 6144 * 2
+    assert mtp.mtp_workspace_bytes(6144, 154880, 16) > mtp.mtp_workspace_bytes(6144, 154880, 1)
+    for bad in [(0, 10, 1), (8, 10, 1), (8208, 10, 1), (24, 10, 1), (16, 0, 1), (16, 10, 0),
+                (16, 10, 65), (16, 2 ** 30 + 1, 1)]:
+        assert mtp.mtp_workspace_bytes(*bad) == 0, bad
+    assert mtp.mtp_workspace_bytes(16, 1, 1) > 0
+    assert mtp.mtp_workspace_bytes(8192, 2 ** 30, 64) > 0
+
+
+def _fake_weights(H=64, V=100, eps=1e-6, **over):
+    base = 0x10000
+    vals = dict(embed=base, enorm_w=base * 2, hnorm_w=base * 3, head_norm_w=base * 4,
+                eh_proj=base * 5, lm_head=base * 6)
+    vals.update(over)
+    return mtp._Weights(H, V, ctypes.c_float(eps), *[vals[k] for k in
+                        ("embed", "enorm_w", "hnorm_w", "head_norm_w", "eh_proj", "lm_head")])
+
+
+def _validate(w, fp8=0, q=0x70000, scale=0x80000, batch=2, tokens=0x90000, hidden=0xA0000,
+              draft=0xB0000, logits=0xC0000, ws=0xD0000, ws_bytes=None):
+    if ws_bytes is None:
+        ws_bytes = mtp.mtp_workspace_bytes(w.hidden, w.vocab, max(batch, 1)) or 1 << 20
+    P = ctypes.c_void_p
+    return mtp.lib().mtp_validate_draft_args(
+        ctypes.byref(w) if w is not None else None, fp8, P(q) if q else None,
+        P(scale) if scale else None, batch, P(tokens) if tokens else None,
+        P(hidden) if hidden else None, P(draft) if draft else None,
+        P(logits) if logits else None, P(ws) if ws else None, ws_bytes)
+
+
+def test_validation_ok():
+    assert _validate(_fake_weights()) == mtp.MTP_OK
+    assert _validate(_fake_weights(), fp8=1) == mtp.MTP_OK
+    assert _validate(_fake_weights(), logits=0) == mtp.MTP_OK          # logits optional
+    assert _validate(_fake_weights(lm_head=0), fp8=1) == mtp.MTP_OK    # FP8 needs no lm_head
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(tokens=0), mtp.MTP_ERR_NULL),
+    (dict(hidden=0), mtp.MTP_ERR_NULL),
+    (dict(draft=0), mtp.MTP_ERR_NULL),
+    (dict(fp8=1, q=0), mtp.MTP_ERR_NULL),
+    (dict(fp8=1, scale=0), mtp.MTP_ERR_NULL),
+    (dict(ws=0), mtp.MTP_ERR_WORKSPACE),
+    (dict(ws_bytes=16), mtp.MTP_ERR_WORKSPACE),
+    (dict(tokens=0x90004), mtp.MTP_ERR_ALIGN),
+    (dict(logits=0xC0002), mtp.MTP_ERR_ALIGN),
+    (dict(ws=0xD0008), mtp.MTP_ERR_ALIGN),
+    (dict(batch=0), mtp.MTP_ERR_SHAPE),
+    (dict(batch=65), mtp.MTP_ERR_SHAPE),
+])
+def test_validation_errors(kw, code):
+    assert _validate(_fake_weights(), **kw) == code
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(H=0), mtp.MTP_ERR_SHAPE), (dict(H=8), mtp.MTP_ERR_SHAPE),
+    (dict(H=40), mtp.MTP_ERR_SHAPE), (dict(H=8208), mtp.MTP_ERR_SHAPE),
+    (dict(V=0), mtp.MTP_ERR_SHAPE), (dict(V=-5), mtp.MTP_ERR_SHAPE),
+    (dict(embed=0), mtp.MTP_ERR_NULL), (dict(eh_proj=0), mtp.MTP_ERR_NULL),
+    (dict(lm_head=0), mtp.MTP_ERR_NULL), (dict(head_norm_w=0x40008), mtp.MTP_ERR_ALIGN),
+])
+def test_validation_weight_errors(over, code):
+    H, V = over.pop("H", 64), over.pop("V", 100)
+    w = _fake_weights(H=H, V=V, **over)
+    assert _validate(w, ws_bytes=1 << 24) == code
+
+
+def test_validation_null_weights():
+    assert _validate(None, ws_bytes=1 << 20) == mtp.MTP_ERR_NULL
+
+
+def test_binding_refuses_host_tensors():
+    """Host tensors never reach the library: the binding raises first."""
+    H, V = 16, 8
+    t = lambda *s: torch.zeros(*s, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        mtp.mtp_weights(t(V, H), t(H), t(H), t(H), t(H, 2 * H), t(V, H), 1e-6)

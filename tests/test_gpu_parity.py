@@ -1,0 +1,250 @@
+"""GPU parity: the HIP path through the C ABI against the FP64 oracle.
+
+Comparison rules (tests/harness.py): FP8 bytes and scales bit-exact; logits
+within 2e-2 sigma (BF16 head) / 6e-2 sigma (FP8 head, against the FP8 oracle);
+drafts exact wherever the oracle's top-1/top-2 gap exceeds twice the
+tolerance, always the lowest index of the GPU's own largest logit, and always in
+the oracle's near-max set.
+
+Shapes: small ones the oracle finishes in seconds (several row tiles, ragged
+column chunks and a ragged vocab), the edge shapes (H = 16, V = 1, H = 8192,
+B = 64), and the full configurations (Mid, Large, Batched) in the launch
+configuration the benchmark times.
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from tests import harness
+
+pytestmark = pytest.mark.gpu
+
+SMALL = [
+    # (hidden, vocab, batch, seed)
+    (256, 4096, 1, 1001),     # the Tiny configuration's shape
+    (1040, 5003, 3, 31),      # ragged column chunk (2 x 512 + 16) and ragged vocab
+    (16, 1, 1, 32),           # smallest hidden, a one-token vocabulary
+    (16, 7, 2, 33),
+    (8192, 2049, 2, 34),      # largest hidden
+    (512, 700, 64, 35),       # largest batch
+    (2064, 1999, 5, 36),
+]
+
+
+def _say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def _check_all(cfg, wts, tokens, hidden, dw, fp8_dev=None, fp8_ref=None, with_logits=True):
+    d, lg = harness.run_draft(dw, tokens, hidden, fp8=fp8_dev, with_logits=with_logits)
+    reps = []
+    for b in range(tokens.size):
+        r = oracle.draft(wts, int(tokens[b]), hidden[b], fp8=fp8_ref)
+        rep = harness.compare_sequence(b, r["o"], None if lg is None else lg[b], int(d[b]),
+                                       r["draft"],
+                                       harness.TOL_FP8 if fp8_ref is not None else harness.TOL_BF16)
+        reps.append(rep)
+        assert rep.ok, (cfg, rep)
+    return d, lg, reps
+
+
+@pytest.mark.parametrize("H,V,B,seed", SMALL)
+def test_small_shapes_bf16_and_fp8(H, V, B, seed):
+    _say(f"\n[parity] H={H} V={V} B={B} seed={seed}")
+    cfg = synth.custom(H, V, B, seed)
+    wts = synth.make_weights(cfg)
+    tokens, hidden = synth.make_inputs(cfg)
+    dw = harness.upload(wts)
+    _check_all(cfg, wts, tokens, hidden, dw)
+    q, s = harness.quantize_dev(dw)
+    ref = oracle.quantize_fp8(wts["lm_head"])
+    assert np.array_equal(q.cpu().numpy(), ref[0])
+    assert np.array_equal(s.cpu().numpy(), ref[1])
+    _check_all(cfg, wts, tokens, hidden, dw, (q, s), ref)
+
+
+def test_quantiser_exhaustive_rows():
+    """Rows [448, w, 0...] for every finite BF16 |w| <= 448 (scale exactly 1)
+    and rows [w, 0...] for every finite nonzero BF16 w (the scale path), plus
+    all-zero and signed-zero rows: GPU codes and scales bit-exact."""
+    _say("\n[quantiser] exhaustive BF16 rows")
+    b = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    f = (b.astype(np.uint32) << 16).view(np.float32)
+    fin = np.isfinite(f)
+    small = b[fin & (np.abs(f) <= 448)]
+    nz = b[fin & (f != 0)]
+    H = 16
+    rows = np.zeros((small.size + nz.size + 2, H), np.uint16)
+    rows[:small.size, 0] = synth.to_bf16(np.float32([448.0]))[0]
+    rows[:small.size, 1] = small
+    rows[small.size:small.size + nz.size, 0] = nz
+    rows[-1, 1::2] = 0x8000
+    ref = oracle.quantize_fp8(rows)
+    V = rows.shape[0]
+    L = harness.to_dev_bf16(rows)
+    q = torch.empty((V, H), dtype=torch.uint8, device="cuda")
+    s = torch.empty(V, dtype=torch.float32, device="cuda")
+    ws = torch.empty(256, dtype=torch.uint8, device="cuda")
+    import mtp_draft_head_embed_amd as mtp
+    mtp.mtp_quantize_head_fp8(L, V, H, q, s, ws)
+    qg, sg = q.cpu().numpy(), s.cpu().numpy()
+    badq = np.nonzero((qg != ref[0]).any(axis=1))[0]
+    assert badq.size == 0, [(hex(rows[i, 0]), hex(rows[i, 1]), qg[i, :2], ref[0][i, :2]) for i in badq[:5]]
+    bads = np.nonzero(sg.view(np.uint32) != ref[1].view(np.uint32))[0]
+    assert bads.size == 0, [(hex(rows[i, 0]), sg[i], ref[1][i]) for i in bads[:5]]
+
+
+def test_quantiser_nonfinite():
+    import mtp_draft_head_embed_amd as mtp
+    for bad in (0x7F80, 0xFF80, 0x7FC0):
+        rows = np.zeros((5, 32), np.uint16)
+        rows[3, 7] = bad
+        L = harness.to_dev_bf16(rows)
+        q = torch.empty((5, 32), dtype=torch.uint8, device="cuda")
+        s = torch.empty(5, dtype=torch.float32, device="cuda")
+        ws = torch.zeros(256, dtype=torch.uint8, device="cuda")
+        with pytest.raises(mtp.MtpError) as ei:
+            mtp.mtp_quantize_head_fp8(L, 5, 32, q, s, ws)
+        assert ei.value.status == mtp.MTP_ERR_NONFINITE
+    # and a clean matrix afterwards reports success (the flag is cleared)
+    rows = synth.normal_bf16(5, 32, 1, "lm_head", 0.0, 0.02)
+    mtp.mtp_quantize_head_fp8(harness.to_dev_bf16(rows), 5, 32, q, s, ws)
+
+
+def test_invalid_tokens_and_no_logits():
+    """tokens >= V give MTP_DRAFT_INVALID for that sequence only; skipping the
+    logits output leaves the drafts unchanged."""
+    _say("\n[invalid tokens]")
+    cfg = synth.custom(512, 3000, 4, 40)
+    wts = synth.make_weights(cfg)
+    tokens, hidden = synth.make_inputs(cfg)
+    tokens[1] = 3000
+    tokens[3] = 0xFFFFFFFF
+    dw = harness.upload(wts)
+    d, lg = harness.run_draft(dw, tokens, hidden)
+    assert d[1] == 0xFFFFFFFF and d[3] == 0xFFFFFFFF
+    for b in (0, 2):
+        r = oracle.draft(wts, int(tokens[b]), hidden[b])
+        rep = harness.compare_sequence(b, r["o"], lg[b], int(d[b]), r["draft"], harness.TOL_BF16)
+        assert rep.ok, rep
+    d2, _ = harness.run_draft(dw, tokens, hidden, with_logits=False)
+    assert np.array_equal(d, d2)
+
+
+def test_determinism_repeat():
+    cfg = synth.custom(1024, 20000, 2, 41)
+    wts = synth.make_weights(cfg)
+    tokens, hidden = synth.make_inputs(cfg)
+    dw = harness.upload(wts)
+    q, s = harness.quantize_dev(dw)
+    for fp8 in (None, (q, s)):
+        a = harness.run_draft(dw, tokens, hidden, fp8=fp8)
+        for _ in range(3):
+            b = harness.run_draft(dw, tokens, hidden, fp8=fp8)
+            assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
+def test_front_and_head_entry_points():
+    """mtp_front's x against the oracle's BF16 x (within one BF16 ulp, the
+    FP32-vs-FP64 rounding of the same sum), then mtp_head_* on the oracle's own
+    x against the oracle head."""
+    import mtp_draft_head_embed_amd as mtp
+    cfg = synth.custom(1536, 9000, 3, 42)
+    wts = synth.make_weights(cfg)
+    tokens, hidden = synth.make_inputs(cfg)
+    dw = harness.upload(wts)
+    B, H, V = 3, 1536, 9000
+    tk = torch.from_numpy(tokens.view(np.int32)).cuda()
+    hd = harness.to_dev_bf16(hidden)
+    x = torch.empty((B, H), dtype=torch.bfloat16, device="cuda")
+    ws = mtp.new_workspace(H, V, B)
+    mtp.mtp_front(dw.w, B, tk, hd, x, ws)
+    torch.cuda.synchronize()
+    xg = harness.bf16_bits(x)
+    q, s = harness.quantize_dev(dw)
+    qref = oracle.quantize_fp8(wts["lm_head"])
+    xs = []
+    for b in range(B):
+        r = oracle.draft(wts, int(tokens[b]), hidden[b])
+        xs.append(r["x"])
+        # BF16 ulps between the two x vectors, on an order-preserving integer key
+        diff = np.abs(harness.bf16_order_key(xg[b]) - harness.bf16_order_key(r["x"]))
+        assert diff.max() <= 1, diff.max()
+        assert np.mean(diff != 0) < 0.01
+    xo = harness.to_dev_bf16(np.stack(xs))
+    for fp8 in (False, True):
+        dr = torch.empty(B, dtype=torch.int32, device="cuda")
+        lg = torch.empty((B, V), dtype=torch.bfloat16, device="cuda")
+        if fp8:
+            mtp.mtp_head_fp8w(dw.w, q, s, B, xo, dr, lg, ws)
+        else:
+            mtp.mtp_head_bf16(dw.w, B, xo, dr, lg, ws)
+        torch.cuda.synchronize()
+        lgb = harness.bf16_bits(lg)
+        d = dr.cpu().numpy().view(np.uint32)
+        for b in range(B):
+            xn = oracle.rmsnorm(xs[b], wts["head_norm_w"], wts["rms_eps"])
+            o = (oracle.gemv_fp8(qref[0], qref[1], xn) if fp8 else oracle.gemv_bf16(wts["lm_head"], xn))
+            od = oracle.argmax_bf16(oracle.bf16_from_f64(o))
+            rep = harness.compare_sequence(b, o, lgb[b], int(d[b]), od,
+                                           harness.TOL_FP8 if fp8 else harness.TOL_BF16)
+            assert rep.ok, rep
+
+
+# ----------------------------------------------------------------------------
+# full-size configurations
+# ----------------------------------------------------------------------------
+
+@pytest.fixture(scope="module")
+def large():
+    cfg = synth.CONFIGS["large"]
+    _say("\n[large] generating weights")
+    wts = synth.make_weights(cfg)
+    return cfg, wts
+
+
+@pytest.mark.slow
+def test_mid_bf16():
+    cfg = synth.CONFIGS["mid"]
+    _say("\n[mid] generating weights")
+    wts = synth.make_weights(cfg)
+    tokens, hidden = synth.make_inputs(cfg)
+    dw = harness.upload(wts)
+    _, _, reps = _check_all(cfg, wts, tokens, hidden, dw)
+    _say(f"[mid] {reps}")
+
+
+@pytest.mark.slow
+def test_large_bf16_and_fp8(large):
+    cfg, wts = large
+    tokens, hidden = synth.make_inputs(cfg)
+    dw = harness.upload(wts)
+    _, _, reps = _check_all(cfg, wts, tokens, hidden, dw)
+    _say(f"[large bf16] {reps}")
+    q, s = harness.quantize_dev(dw)
+    ref = oracle.quantize_fp8(wts["lm_head"])
+    assert np.array_equal(q.cpu().numpy(), ref[0])
+    assert np.array_equal(s.cpu().numpy(), ref[1])
+    _, _, reps = _check_all(cfg, wts, tokens, hidden, dw, (q, s), ref)
+    _say(f"[large fp8] {reps}")
+
+
+@pytest.mark.slow
+def test_batched_fp8():
+    """B = 16 distinct tokens, FP8 head (the batched configuration)."""
+    cfg = synth.CONFIGS["batched"]
+    _say("\n[batched] generating weights")
+    wts = synth.make_weights(cfg)
+    tokens, hidden = synth.make_inputs(cfg)
+    assert len(set(tokens.tolist())) == 16
+    dw = harness.upload(wts)
+    q, s = harness.quantize_dev(dw)
+    ref = oracle.quantize_fp8(wts["lm_head"])
+    assert np.array_equal(q.cpu().numpy(), ref[0])
+    _, _, reps = _check_all(cfg, wts, tokens, hidden, dw, (q, s), ref)
+    _say(f"[batched fp8] max err {max(r.max_err for r in reps):.4g}")
