@@ -151,7 +151,9 @@ def main():
         "unit": "GB/s",
         "frac": round(r["lm_head_GBps"] / HBM_PEAK_GBPS, 4),
         "traffic": None,
-        "kernel": "row_gemv_kernel (lm_head, BF16) + argmax_final_kernel",
+        "kernel": "row_gemv_kernel<BF16, head-norm prologue, argmax-partials epilogue>; the "
+                  "timed mtp_head_bf16 call also runs the one-workgroup-per-sequence "
+                  "argmax_final_kernel after it",
         "algorithmic_bytes_per_launch": hb,
         "avg_launch_us": round(r["head_us"], 2),
     }

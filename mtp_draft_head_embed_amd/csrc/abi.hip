@@ -115,26 +115,26 @@ RowGemvArgs front_args(const mtp_weights *w, const uint32_t *tokens, const void 
     return a;
 }
 
+// The head sweep: norm, lm_head and argmax partials, then the final argmax.
 int run_head(const mtp_weights *w, bool fp8, const uint8_t *q, const float *scale, int32_t batch,
              const void *x, const uint32_t *tokens, uint32_t *draft, void *logits, void *ws,
              hipStream_t s)
 {
     const WsLayout L = ws_layout(w->hidden, batch);
-    Partial *parts = reinterpret_cast<Partial *>(static_cast<char *>(ws) + L.part_off);
     RowGemvArgs a{};
     a.W = fp8 ? static_cast<const void *>(q) : w->lm_head;
     a.scale = scale;
     a.N = w->vocab;
     a.K = w->hidden;
+    a.vocab = w->vocab;
+    a.tokens = tokens;
     a.xin = static_cast<const uint16_t *>(x);
     a.norm_w = static_cast<const uint16_t *>(w->head_norm_w);
     a.eps = w->rms_eps;
     a.logits = static_cast<uint16_t *>(logits);
-    a.partials = parts;
-    const int grid = head_grid(w->vocab, device_cu_count());
-    if (launch_head(a, fp8, grid, batch, s) != hipSuccess)
-        return MTP_ERR_HIP;
-    if (launch_argmax_final(parts, grid, tokens, w->vocab, draft, batch, s) != hipSuccess)
+    a.partials = reinterpret_cast<Partial *>(static_cast<char *>(ws) + L.part_off);
+    a.draft = draft;
+    if (launch_head(a, fp8, batch, s) != hipSuccess)
         return MTP_ERR_HIP;
     return MTP_OK;
 }

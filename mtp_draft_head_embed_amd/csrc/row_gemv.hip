@@ -1,33 +1,42 @@
 // row_gemv.hip -- bandwidth-bound GEMV over row-major weights, one wavefront
 // per output row, for the single-sequence draft sweep on gfx950.
 //
-// Covers three steps of `forward_one` (metrale_model_arch/glm5next_mtp_head.rs):
+// Covers these steps of `forward_one` (metrale_model_arch/glm5next_mtp_head.rs):
 //   * eh_proj:  x = BF16(eh_proj . [enorm(embed[token]) | hnorm(hidden)]).
-//     The gather and both vanilla norms run as this kernel's prologue (each
-//     workgroup rebuilds the [2H] concat in LDS), so no separate norm launches.
-//   * lm_head, BF16 (`dense_gemv`) and FP8 (`dense_gemv_fp8w`): the
-//     `shared_head.norm` of x runs as the prologue (the normed BF16 vector is
-//     staged in LDS) and the argmax runs as the epilogue: every logit is rounded
-//     to BF16, optionally stored, and each workgroup leaves its best (value,
-//     index) in a partials array that argmax_final reduces.
+//     The embedding-row gather and both vanilla norms run as this kernel's
+//     prologue (each workgroup rebuilds the [2H] concat in LDS), so there are
+//     no separate norm launches.
+//   * lm_head, BF16 (`dense_gemv`) and FP8 (`dense_gemv_fp8w`), with the
+//     `shared_head.norm` of x as the prologue (the normed BF16 vector staged in
+//     LDS) and the first argmax stage (`argmax_bf16`) as the epilogue: every
+//     logit is rounded to BF16 and optionally stored, and each workgroup leaves
+//     its best (value, index) in a partials array; argmax_final_kernel, one
+//     workgroup per sequence, reduces them.  (A last-workgroup-done fusion of
+//     the two stages needs agent-scope release/acquire, which on gfx950 writes
+//     back and invalidates the XCD's whole L2 in every workgroup: measured at
+//     +35-55 us per sweep, against 1-3 us for the second launch.)
 //
 // Memory pattern: lane l of a wave reads 16 contiguous bytes at column
 // c*CW + l*EPL of its row (CW = 64 lanes x EPL elements), so each load
 // instruction of a wave fetches 1 KiB of one row; RPI rows x U chunks are in
-// flight per wave.  Rows are dealt to the waves of the whole grid round-robin,
-// so at any moment the grid streams one contiguous window of the matrix.  The
-// activation vector is read from LDS (BF16), once per 16-byte weight chunk.
+// flight per wave, with the non-temporal hint (each weight byte is read once
+// per sweep).  Rows are dealt to the waves of the whole grid round-robin, so
+// at any moment the grid streams one contiguous window of the matrix.  The
+// first group of loads is issued before the prologue so HBM is busy while the
+// norms are computed.  Grids are a multiple of the CU count so every CU gets
+// the same number of workgroups.
 //
 // Sums are FP32 in a fixed order (per lane over its chunks, then a fixed xor
-// butterfly), so results do not depend on grid size or timing.
+// butterfly), so results do not depend on grid size or timing; the argmax
+// order (value, then lower index) is associative, so neither does the draft.
 #include "common.hpp"
 #include "kernels.hpp"
 
 namespace mtp {
 
-// Sum of squares of a BF16 vector of n elements (n % 8 == 0, n <= 8192),
-// reduced over the whole workgroup in a fixed order.  `v` receives the
-// thread's 16-byte pieces (element (i*blockDim + tid)*8) for reuse.
+// Sum of squares of a BF16 vector of n elements (n % 8 == 0,
+// n <= 4 * blockDim * 8), reduced over the whole workgroup in a fixed order.
+// `v` receives the thread's 16-byte pieces (element (i*blockDim + tid)*8).
 __device__ __forceinline__ float block_sumsq(const uint16_t *__restrict__ src, int n, bool valid,
                                              uint4 (&v)[4], float *red)
 {
@@ -111,8 +120,22 @@ __device__ __forceinline__ float dot4_fp8(uint32_t q, uint32_t a01, uint32_t a23
     return acc;
 }
 
-template <bool FP8, int PRO, int EPI, int RPI, int U>
-__global__ __launch_bounds__(256) void row_gemv_kernel(RowGemvArgs a)
+// Weight stream loads.  With NT the load carries the non-temporal hint: the
+// weights are read once per sweep, so they should not displace the cached
+// activations and workspace.
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+template <bool NT>
+__device__ __forceinline__ uint4 ld_weights(const char *p)
+{
+    if (NT) {
+        const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));
+        return make_uint4(v.x, v.y, v.z, v.w);
+    }
+    return *reinterpret_cast<const uint4 *>(p);
+}
+
+template <bool FP8, int PRO, int EPI, int RPI, int U, bool NT = true, int BS = 256>
+__global__ __launch_bounds__(BS) void row_gemv_kernel(RowGemvArgs a)
 {
     extern __shared__ uint4 lds_raw[];
     __shared__ float red[16];
@@ -125,6 +148,43 @@ __global__ __launch_bounds__(256) void row_gemv_kernel(RowGemvArgs a)
     const int lane = tid & (kWave - 1);
     const int wid = tid / kWave;
     const int K = a.K;
+
+    constexpr int EPL = FP8 ? 16 : 8;  // elements per 16-byte load
+    constexpr int CW = kWave * EPL;    // columns per wave-wide load
+    constexpr int ESZ = FP8 ? 1 : 2;   // bytes per weight element
+    const int nchunks = (K + CW - 1) / CW;
+    const int wpb = BS / kWave;
+    const int Wt = gridDim.x * wpb;
+    const int gw = blockIdx.x * wpb + wid;
+    const int N = a.N;
+    const char *Wb = reinterpret_cast<const char *>(a.W);
+
+    // Row ownership: interleaved (row r goes to wave r mod Wt) or, with
+    // a.contig_rows > 0, contiguous blocks of that many rows per wave.
+    int r_begin = gw, r_end = N, r_inner = Wt;
+    if (a.contig_rows > 0) {
+        r_begin = gw * a.contig_rows;
+        r_end = min(N, r_begin + a.contig_rows);
+        r_inner = 1;
+    }
+    const int r_outer = r_inner * RPI;
+
+    uint4 wv[RPI][U];
+    auto load_group = [&](int r0, int c0) {
+#pragma unroll
+        for (int k = 0; k < RPI; ++k) {
+            const int r = r0 + k * r_inner;
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int col = (c0 + u) * CW + lane * EPL;
+                wv[k][u] = make_uint4(0, 0, 0, 0);
+                if (r < r_end && col < K)
+                    wv[k][u] = ld_weights<NT>(Wb + (size_t(r) * size_t(K) + size_t(col)) * ESZ);
+            }
+        }
+    };
+    // the first group's loads do not depend on the activation: issue them now
+    load_group(r_begin, 0);
 
     // ---- prologue: the BF16 activation vector act[0..K) in LDS -------------
     if (PRO == PRO_FRONT) {
@@ -147,38 +207,19 @@ __global__ __launch_bounds__(256) void row_gemv_kernel(RowGemvArgs a)
     __syncthreads();
 
     // ---- row sweep ---------------------------------------------------------
-    constexpr int EPL = FP8 ? 16 : 8;       // elements per 16-byte load
-    constexpr int CW = kWave * EPL;         // columns per wave-wide load
-    constexpr int ESZ = FP8 ? 1 : 2;        // bytes per weight element
-    const int nchunks = (K + CW - 1) / CW;
-    const int wpb = blockDim.x / kWave;
-    const int Wt = gridDim.x * wpb;
-    const int gw = blockIdx.x * wpb + wid;
-    const int N = a.N;
-    const char *Wb = reinterpret_cast<const char *>(a.W);
-
     float best_v = -INFINITY;
     uint32_t best_i = 0xFFFFFFFFu;
+    bool have_group = true;
 
-    for (int r0 = gw; r0 < N; r0 += Wt * RPI) {
+    for (int r0 = r_begin; r0 < r_end; r0 += r_outer) {
         float acc[RPI];
 #pragma unroll
         for (int k = 0; k < RPI; ++k)
             acc[k] = 0.f;
         for (int c0 = 0; c0 < nchunks; c0 += U) {
-            uint4 wv[RPI][U];
-#pragma unroll
-            for (int k = 0; k < RPI; ++k) {
-                const int r = r0 + k * Wt;
-#pragma unroll
-                for (int u = 0; u < U; ++u) {
-                    const int col = (c0 + u) * CW + lane * EPL;
-                    wv[k][u] = make_uint4(0, 0, 0, 0);
-                    if (r < N && col < K)
-                        wv[k][u] = *reinterpret_cast<const uint4 *>(
-                            Wb + (size_t(r) * size_t(K) + size_t(col)) * ESZ);
-                }
-            }
+            if (!have_group)
+                load_group(r0, c0);
+            have_group = false;
 #pragma unroll
             for (int u = 0; u < U; ++u) {
                 const int col = (c0 + u) * CW + lane * EPL;
@@ -206,9 +247,9 @@ __global__ __launch_bounds__(256) void row_gemv_kernel(RowGemvArgs a)
         }
 #pragma unroll
         for (int k = 0; k < RPI; ++k) {
-            const int r = r0 + k * Wt;
+            const int r = r0 + k * r_inner;
             const float sum = wave_sum(acc[k]);
-            if (r < N) {
+            if (r < r_end) {
                 if (EPI == EPI_STORE) {
                     if (lane == 0)
                         a.out[size_t(b) * N + r] = uint16_t(f32_to_bf16_bits(sum));
@@ -247,7 +288,9 @@ __global__ __launch_bounds__(256) void row_gemv_kernel(RowGemvArgs a)
     }
 }
 
-// Second argmax stage: one workgroup per sequence reduces its partials.
+// Second argmax stage: one workgroup per sequence reduces its partials and
+// writes the draft (MTP_DRAFT_INVALID when the sequence's token is out of
+// range).
 __global__ __launch_bounds__(256) void argmax_final_kernel(const Partial *__restrict__ partials,
                                                            int nparts, const uint32_t *tokens,
                                                            int vocab, uint32_t *draft)
@@ -272,12 +315,12 @@ __global__ __launch_bounds__(256) void argmax_final_kernel(const Partial *__rest
     }
     __syncthreads();
     if (tid == 0) {
+        // wave 0's result is already in (bv, bi)
         for (int w = 1; w < int(blockDim.x / kWave); ++w)
             if (better(sv[w], si[w], bv, bi)) {
                 bv = sv[w];
                 bi = si[w];
             }
-        // wave 0's value is in bv already (lane 0 of wave 0 is tid 0)
         if (tokens && tokens[b] >= uint32_t(vocab))
             bi = 0xFFFFFFFFu;
         draft[b] = bi;
@@ -289,8 +332,11 @@ __global__ __launch_bounds__(256) void argmax_final_kernel(const Partial *__rest
 // ---------------------------------------------------------------------------
 
 template <bool FP8, int PRO, int EPI, int RPI, int U>
-static hipError_t launch_one(const RowGemvArgs &a, int grid, int batch, hipStream_t s)
+static hipError_t launch_one(const RowGemvArgs &a, int grid, int batch, hipStream_t s,
+                             int *grid_out)
 {
+    if (grid_out)
+        *grid_out = grid;
     const size_t lds = align256(size_t(a.K) * 2);
     hipLaunchKernelGGL((row_gemv_kernel<FP8, PRO, EPI, RPI, U>), dim3(grid, batch), dim3(256),
                        lds, s, a);
@@ -307,42 +353,71 @@ int device_cu_count()
     return n;
 }
 
-hipError_t launch_eh_proj(const RowGemvArgs &a, int batch, hipStream_t s)
+// Workgroups: `per_cu` per CU (so every CU carries the same load), but no
+// more than the rows need (4 waves x rpi rows per workgroup pass).
+static int grid_for(int N, int rpi, int per_cu, int cu_count)
 {
-    // RPI = 2 rows per wave pass, 4 waves per workgroup: one pass over N rows
-    // needs N / 8 workgroups; a few passes per wave keep the grid resident.
-    const int waves = (a.N + 1) / 2;
-    int grid = (waves + 3) / 4;
-    if (grid > kMaxHeadBlocks)
-        grid = kMaxHeadBlocks;
-    return launch_one<false, PRO_FRONT, EPI_STORE, 2, 8>(a, grid, batch, s);
-}
-
-int head_grid(int N, int cu_count)
-{
-    int grid = cu_count * 4;
-    const int need = (N + 7) / 8;
+    int grid = cu_count * per_cu;
+    const int need = (N + 4 * rpi - 1) / (4 * rpi);
     if (grid > need)
         grid = need;
     if (grid > kMaxHeadBlocks)
         grid = kMaxHeadBlocks;
-    if (grid < 1)
-        grid = 1;
-    return grid;
+    return grid < 1 ? 1 : grid;
 }
 
-hipError_t launch_head(const RowGemvArgs &a, bool fp8, int grid, int batch, hipStream_t s)
+// BF16 weights: 512 columns per wave-wide load.  U = chunks per row held in
+// flight (the whole row when it fits), RPI = rows per wave pass.
+template <int PRO, int EPI>
+static hipError_t launch_bf16(const RowGemvArgs &a, int per_cu, int batch, hipStream_t s, int cus,
+                              int *grid_out)
 {
-    if (fp8)
-        return launch_one<true, PRO_HEADNORM, EPI_ARGMAX, 4, 4>(a, grid, batch, s);
-    return launch_one<false, PRO_HEADNORM, EPI_ARGMAX, 2, 8>(a, grid, batch, s);
+    const int nch = (a.K + 511) / 512;
+#define MTP_BF16(RPI, U) \
+    return launch_one<false, PRO, EPI, RPI, U>(a, grid_for(a.N, RPI, per_cu, cus), batch, s, \
+                                               grid_out)
+    if (nch <= 1) MTP_BF16(4, 1);
+    if (nch <= 2) MTP_BF16(4, 2);
+    if (nch <= 4) MTP_BF16(2, 4);
+    if (nch <= 8) MTP_BF16(2, 8);
+    if (nch <= 12) MTP_BF16(1, 12);
+    if (nch <= 16) MTP_BF16(1, 16);
+    if (nch <= 24) MTP_BF16(1, 24);
+    MTP_BF16(1, 16);
+#undef MTP_BF16
 }
 
-hipError_t launch_argmax_final(const Partial *partials, int nparts, const uint32_t *tokens,
-                               int vocab, uint32_t *draft, int batch, hipStream_t s)
+// FP8 codes: 1024 columns per wave-wide load.
+static hipError_t launch_fp8_head(const RowGemvArgs &a, int per_cu, int batch, hipStream_t s,
+                                  int cus, int *grid_out)
 {
-    hipLaunchKernelGGL(argmax_final_kernel, dim3(batch), dim3(256), 0, s, partials, nparts,
-                       tokens, vocab, draft);
+    const int nch = (a.K + 1023) / 1024;
+#define MTP_FP8(RPI, U)                                                                         \
+    return launch_one<true, PRO_HEADNORM, EPI_ARGMAX, RPI, U>(a, grid_for(a.N, RPI, per_cu, cus), \
+                                                               batch, s, grid_out)
+    if (nch <= 1) MTP_FP8(4, 1);
+    if (nch <= 2) MTP_FP8(4, 2);
+    if (nch <= 4) MTP_FP8(2, 4);
+    if (nch <= 6) MTP_FP8(2, 6);
+    MTP_FP8(2, 8);
+#undef MTP_FP8
+}
+
+hipError_t launch_eh_proj(const RowGemvArgs &a, int batch, hipStream_t s)
+{
+    return launch_bf16<PRO_FRONT, EPI_STORE>(a, 2, batch, s, device_cu_count(), nullptr);
+}
+
+hipError_t launch_head(const RowGemvArgs &a, bool fp8, int batch, hipStream_t s)
+{
+    const int cus = device_cu_count();
+    int grid = 0;
+    const hipError_t e = fp8 ? launch_fp8_head(a, 3, batch, s, cus, &grid)
+                             : launch_bf16<PRO_HEADNORM, EPI_ARGMAX>(a, 2, batch, s, cus, &grid);
+    if (e != hipSuccess)
+        return e;
+    hipLaunchKernelGGL(argmax_final_kernel, dim3(batch), dim3(256), 0, s, a.partials, grid,
+                       a.tokens, a.vocab, a.draft);
     return hipGetLastError();
 }
 
