@@ -115,12 +115,92 @@ RowGemvArgs front_args(const mtp_weights *w, const uint32_t *tokens, const void 
     return a;
 }
 
-// The head sweep: norm, lm_head and argmax partials, then the final argmax.
+char *ws_at(void *ws, size_t off) { return static_cast<char *>(ws) + off; }
+
+// Batched front half: concat rows, eh_proj on MFMA with split-K partial sums,
+// then x = BF16(sum of splits) and, when xn is wanted, the head norm of x.
+int run_front_batched(const mtp_weights *w, int32_t batch, const uint32_t *tokens,
+                      const void *hidden, void *x, void *xn, void *ws, hipStream_t s)
+{
+    const WsLayout L = ws_layout(w->hidden, batch);
+    const int H = w->hidden;
+    FrontArgs f{};
+    f.embed = static_cast<const uint16_t *>(w->embed);
+    f.vocab = w->vocab;
+    f.H = H;
+    f.tokens = tokens;
+    f.hidden = static_cast<const uint16_t *>(hidden);
+    f.enorm_w = static_cast<const uint16_t *>(w->enorm_w);
+    f.hnorm_w = static_cast<const uint16_t *>(w->hnorm_w);
+    f.eps = w->rms_eps;
+    f.concat = reinterpret_cast<uint16_t *>(ws_at(ws, L.concat_off));
+    if (launch_front_concat(f, batch, s) != hipSuccess)
+        return MTP_ERR_HIP;
+    MfmaArgs m{};
+    m.W = w->eh_proj;
+    m.N = H;
+    m.K = 2 * H;
+    m.A = f.concat;
+    m.B = batch;
+    m.out_f32 = reinterpret_cast<float *>(ws_at(ws, L.p_off));
+    if (launch_eh_proj_mfma(m, s) != hipSuccess)
+        return MTP_ERR_HIP;
+    SumNormArgs r{};
+    r.P = m.out_f32;
+    r.S = eh_split(H).S;
+    r.B = batch;
+    r.H = H;
+    r.x_out = static_cast<uint16_t *>(x);
+    r.norm_w = static_cast<const uint16_t *>(w->head_norm_w);
+    r.eps = w->rms_eps;
+    r.xn_out = static_cast<uint16_t *>(xn);
+    if (launch_sum_norm(r, batch, s) != hipSuccess)
+        return MTP_ERR_HIP;
+    return MTP_OK;
+}
+
+// Batched head: lm_head on MFMA over the normed xn, then the final argmax.
+int run_head_batched(const mtp_weights *w, bool fp8, const uint8_t *q, const float *scale,
+                     int32_t batch, const void *xn, const uint32_t *tokens, uint32_t *draft,
+                     void *logits, void *ws, hipStream_t s)
+{
+    const WsLayout L = ws_layout(w->hidden, batch);
+    MfmaArgs m{};
+    m.W = fp8 ? static_cast<const void *>(q) : w->lm_head;
+    m.scale = scale;
+    m.N = w->vocab;
+    m.K = w->hidden;
+    m.A = static_cast<const uint16_t *>(xn);
+    m.B = batch;
+    m.logits = static_cast<uint16_t *>(logits);
+    m.partials = reinterpret_cast<Partial *>(ws_at(ws, L.part_off));
+    int grid = 0;
+    if (launch_head_mfma(m, fp8, &grid, s) != hipSuccess)
+        return MTP_ERR_HIP;
+    if (launch_argmax_final(m.partials, grid, tokens, w->vocab, draft, batch, s) != hipSuccess)
+        return MTP_ERR_HIP;
+    return MTP_OK;
+}
+
+// The head sweep from a block output x: norm, lm_head, argmax.
 int run_head(const mtp_weights *w, bool fp8, const uint8_t *q, const float *scale, int32_t batch,
              const void *x, const uint32_t *tokens, uint32_t *draft, void *logits, void *ws,
              hipStream_t s)
 {
     const WsLayout L = ws_layout(w->hidden, batch);
+    if (batch > 1) {
+        SumNormArgs r{};
+        r.S = 0;
+        r.B = batch;
+        r.H = w->hidden;
+        r.x_in = static_cast<const uint16_t *>(x);
+        r.norm_w = static_cast<const uint16_t *>(w->head_norm_w);
+        r.eps = w->rms_eps;
+        r.xn_out = reinterpret_cast<uint16_t *>(ws_at(ws, L.xn_off));
+        if (launch_sum_norm(r, batch, s) != hipSuccess)
+            return MTP_ERR_HIP;
+        return run_head_batched(w, fp8, q, scale, batch, r.xn_out, tokens, draft, logits, ws, s);
+    }
     RowGemvArgs a{};
     a.W = fp8 ? static_cast<const void *>(q) : w->lm_head;
     a.scale = scale;
@@ -132,7 +212,7 @@ int run_head(const mtp_weights *w, bool fp8, const uint8_t *q, const float *scal
     a.norm_w = static_cast<const uint16_t *>(w->head_norm_w);
     a.eps = w->rms_eps;
     a.logits = static_cast<uint16_t *>(logits);
-    a.partials = reinterpret_cast<Partial *>(static_cast<char *>(ws) + L.part_off);
+    a.partials = reinterpret_cast<Partial *>(ws_at(ws, L.part_off));
     a.draft = draft;
     if (launch_head(a, fp8, batch, s) != hipSuccess)
         return MTP_ERR_HIP;
@@ -146,7 +226,12 @@ int run_draft(const mtp_weights *w, bool fp8, const uint8_t *q, const float *sca
     MTP_TRY(validate_draft(w, fp8, q, scale, batch, tokens, hidden, draft, logits, ws, ws_bytes));
     hipStream_t s = static_cast<hipStream_t>(stream);
     const WsLayout L = ws_layout(w->hidden, batch);
-    void *x = static_cast<char *>(ws) + L.x_off;
+    void *x = ws_at(ws, L.x_off);
+    if (batch > 1) {
+        void *xn = ws_at(ws, L.xn_off);
+        MTP_TRY(run_front_batched(w, batch, tokens, hidden, x, xn, ws, s));
+        return run_head_batched(w, fp8, q, scale, batch, xn, tokens, draft, logits, ws, s);
+    }
     if (launch_eh_proj(front_args(w, tokens, hidden, x), batch, s) != hipSuccess)
         return MTP_ERR_HIP;
     return run_head(w, fp8, q, scale, batch, x, tokens, draft, logits, ws, s);
@@ -216,6 +301,8 @@ int mtp_front(const mtp_weights *w, int32_t batch, const uint32_t *tokens, const
     MTP_TRY(validate_front(w, batch, tokens, hidden, x));
     MTP_TRY(check_ws(workspace, ws_bytes, w->hidden, batch));
     hipStream_t s = static_cast<hipStream_t>(stream);
+    if (batch > 1)
+        return run_front_batched(w, batch, tokens, hidden, x, nullptr, workspace, s);
     if (launch_eh_proj(front_args(w, tokens, hidden, x), batch, s) != hipSuccess)
         return MTP_ERR_HIP;
     return MTP_OK;

@@ -16,6 +16,9 @@ constexpr int kWave = 64;
 // Workspace layout (all offsets 256-byte aligned).
 //   x        BF16 [B][H]        block input, written by the front half
 //   partials (f32 value, u32 index) [B][kMaxHeadBlocks]  per-workgroup argmax
+//   concat   BF16 [B][2H]       batched path: [enorm(e) | hnorm(h)]
+//   xn       BF16 [B][H]        batched path: shared_head.norm(x)
+//   P        FP32 [S][B][H]     batched path: eh_proj split-K partial sums
 // ---------------------------------------------------------------------------
 constexpr int kMaxHeadBlocks = 4096;
 
@@ -29,17 +32,30 @@ inline size_t align256(size_t n) { return (n + 255) & ~size_t(255); }
 struct WsLayout {
     size_t x_off, x_bytes;
     size_t part_off, part_bytes;
+    size_t concat_off, xn_off, p_off;
     size_t total;
 };
+
+// eh_proj K-splits of the batched path for this hidden size (mfma_gemm.hip).
+int eh_split_count(int hidden);
 
 inline WsLayout ws_layout(int hidden, int batch)
 {
     WsLayout L;
+    const size_t bh = size_t(batch) * size_t(hidden);
     L.x_off = 0;
-    L.x_bytes = align256(size_t(batch) * size_t(hidden) * 2);
+    L.x_bytes = align256(bh * 2);
     L.part_off = L.x_off + L.x_bytes;
     L.part_bytes = align256(size_t(batch) * kMaxHeadBlocks * sizeof(Partial));
     L.total = L.part_off + L.part_bytes;
+    if (batch > 1) {
+        L.concat_off = L.total;
+        L.xn_off = L.concat_off + align256(bh * 4);
+        L.p_off = L.xn_off + align256(bh * 2);
+        L.total = L.p_off + align256(size_t(eh_split_count(hidden)) * bh * 4);
+    } else {
+        L.concat_off = L.xn_off = L.p_off = 0;
+    }
     return L;
 }
 
@@ -96,6 +112,68 @@ __device__ __forceinline__ void wave_argmax(float &v, uint32_t &i)
         if (better(ov, oi, v, i)) {
             v = ov;
             i = oi;
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Vanilla RMSNorm pieces (x * w / sqrt(mean(x^2) + eps)) for one workgroup
+// holding one BF16 vector; thread t owns elements (i*blockDim + t)*8 .. +8.
+// ---------------------------------------------------------------------------
+// Sum of squares of a BF16 vector of n elements (n % 8 == 0,
+// n <= 4 * blockDim * 8), reduced over the whole workgroup in a fixed order.
+// `v` receives the thread's 16-byte pieces (element (i*blockDim + tid)*8).
+__device__ __forceinline__ float block_sumsq(const uint16_t *__restrict__ src, int n, bool valid,
+                                             uint4 (&v)[4], float *red)
+{
+    const int tid = threadIdx.x;
+    float ss = 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int j = (i * blockDim.x + tid) * 8;
+        v[i] = make_uint4(0, 0, 0, 0);
+        if (valid && j < n)
+            v[i] = *reinterpret_cast<const uint4 *>(src + j);
+        const uint32_t w[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const float a = bf16_lo(w[q]), b = bf16_hi(w[q]);
+            ss = fmaf(a, a, ss);
+            ss = fmaf(b, b, ss);
+        }
+    }
+    ss = wave_sum(ss);
+    const int nw = blockDim.x / kWave;
+    __syncthreads();
+    if ((tid & (kWave - 1)) == 0)
+        red[tid / kWave] = ss;
+    __syncthreads();
+    float tot = 0.f;
+    for (int w = 0; w < nw; ++w)
+        tot += red[w];
+    return tot;
+}
+
+// out[j] = BF16(x_j * w_j / r) for the thread's pieces (dst in LDS or global).
+__device__ __forceinline__ void norm_to_lds(const uint4 (&v)[4], const uint16_t *__restrict__ w,
+                                            int n, float r, uint16_t *dst)
+{
+    const int tid = threadIdx.x;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int j = (i * blockDim.x + tid) * 8;
+        if (j < n) {
+            const uint4 wv = *reinterpret_cast<const uint4 *>(w + j);
+            const uint32_t xa[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
+            const uint32_t wa[4] = {wv.x, wv.y, wv.z, wv.w};
+            uint32_t o[4];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const float lo = (bf16_lo(xa[q]) * bf16_lo(wa[q])) / r;
+                const float hi = (bf16_hi(xa[q]) * bf16_hi(wa[q])) / r;
+                o[q] = pack_bf16x2(lo, hi);
+            }
+            *reinterpret_cast<uint4 *>(dst + j) = make_uint4(o[0], o[1], o[2], o[3]);
         }
     }
 }

@@ -34,6 +34,46 @@ struct RowGemvArgs {
     uint32_t *draft;      // EPI_ARGMAX: [B] argmax, or MTP_DRAFT_INVALID
 };
 
+// Batched (B >= 2) GEMM on MFMA: Y[b][n] = sum_k A[b][k] W[n][k].
+struct MfmaArgs {
+    const void *W;        // [N][K] BF16, or E4M3FN codes (lm_head FP8 copy)
+    const float *scale;   // [N] per-row scale (FP8 head)
+    int N, K;
+    const uint16_t *A;    // [B][K] BF16 activations
+    int B;
+    int Ks;               // K columns per split (grid.y splits)
+    int KC;               // K columns per LDS chunk (set by the launcher)
+    float *out_f32;       // EPI_STORE: [splits][B][N] FP32 partial sums
+    uint16_t *logits;     // EPI_ARGMAX: [B][N] BF16 or null
+    Partial *partials;    // EPI_ARGMAX: [B][kMaxHeadBlocks]
+};
+
+// eh_proj K-split for the batched path: S splits of Ks columns.
+struct EhSplit {
+    int S, Ks;
+};
+EhSplit eh_split(int hidden);
+
+struct FrontArgs {
+    const uint16_t *embed;
+    int vocab, H;
+    const uint32_t *tokens;
+    const uint16_t *hidden;
+    const uint16_t *enorm_w, *hnorm_w;
+    float eps;
+    uint16_t *concat;     // [B][2H]
+};
+
+struct SumNormArgs {
+    const float *P;       // [S][B][H] eh_proj partial sums (S > 0), or
+    int S, B, H;
+    const uint16_t *x_in; // [B][H] block output (S == 0)
+    uint16_t *x_out;      // [B][H] BF16 x, or null
+    const uint16_t *norm_w;
+    float eps;
+    uint16_t *xn_out;     // [B][H] BF16 normed x, or null
+};
+
 int device_cu_count();
 
 // eh_proj with the fused gather + dual norm prologue.
@@ -44,5 +84,12 @@ hipError_t launch_head(const RowGemvArgs &a, bool fp8, int batch, hipStream_t s)
 
 hipError_t launch_quantize(const uint16_t *L, int V, int H, uint8_t *q, float *scale,
                            uint32_t *flag, hipStream_t s);
+
+hipError_t launch_front_concat(const FrontArgs &a, int batch, hipStream_t s);
+hipError_t launch_sum_norm(const SumNormArgs &a, int batch, hipStream_t s);
+hipError_t launch_eh_proj_mfma(const MfmaArgs &a, hipStream_t s);
+hipError_t launch_head_mfma(const MfmaArgs &a, bool fp8, int *grid_out, hipStream_t s);
+hipError_t launch_argmax_final(const Partial *partials, int nparts, const uint32_t *tokens,
+                               int vocab, uint32_t *draft, int batch, hipStream_t s);
 
 }  // namespace mtp

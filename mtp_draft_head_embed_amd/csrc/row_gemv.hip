@@ -34,64 +34,6 @@
 
 namespace mtp {
 
-// Sum of squares of a BF16 vector of n elements (n % 8 == 0,
-// n <= 4 * blockDim * 8), reduced over the whole workgroup in a fixed order.
-// `v` receives the thread's 16-byte pieces (element (i*blockDim + tid)*8).
-__device__ __forceinline__ float block_sumsq(const uint16_t *__restrict__ src, int n, bool valid,
-                                             uint4 (&v)[4], float *red)
-{
-    const int tid = threadIdx.x;
-    float ss = 0.f;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int j = (i * blockDim.x + tid) * 8;
-        v[i] = make_uint4(0, 0, 0, 0);
-        if (valid && j < n)
-            v[i] = *reinterpret_cast<const uint4 *>(src + j);
-        const uint32_t w[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const float a = bf16_lo(w[q]), b = bf16_hi(w[q]);
-            ss = fmaf(a, a, ss);
-            ss = fmaf(b, b, ss);
-        }
-    }
-    ss = wave_sum(ss);
-    const int nw = blockDim.x / kWave;
-    __syncthreads();
-    if ((tid & (kWave - 1)) == 0)
-        red[tid / kWave] = ss;
-    __syncthreads();
-    float tot = 0.f;
-    for (int w = 0; w < nw; ++w)
-        tot += red[w];
-    return tot;
-}
-
-// out[j] = BF16(x_j * w_j / r) for the thread's pieces, written to LDS.
-__device__ __forceinline__ void norm_to_lds(const uint4 (&v)[4], const uint16_t *__restrict__ w,
-                                            int n, float r, uint16_t *dst)
-{
-    const int tid = threadIdx.x;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int j = (i * blockDim.x + tid) * 8;
-        if (j < n) {
-            const uint4 wv = *reinterpret_cast<const uint4 *>(w + j);
-            const uint32_t xa[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
-            const uint32_t wa[4] = {wv.x, wv.y, wv.z, wv.w};
-            uint32_t o[4];
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const float lo = (bf16_lo(xa[q]) * bf16_lo(wa[q])) / r;
-                const float hi = (bf16_hi(xa[q]) * bf16_hi(wa[q])) / r;
-                o[q] = pack_bf16x2(lo, hi);
-            }
-            *reinterpret_cast<uint4 *>(dst + j) = make_uint4(o[0], o[1], o[2], o[3]);
-        }
-    }
-}
-
 // Dot of 8 BF16 weights with 8 BF16 activations, accumulated in order.
 __device__ __forceinline__ float dot8_bf16(const uint4 &w, const uint4 &a, float acc)
 {
@@ -416,8 +358,14 @@ hipError_t launch_head(const RowGemvArgs &a, bool fp8, int batch, hipStream_t s)
                              : launch_bf16<PRO_HEADNORM, EPI_ARGMAX>(a, 2, batch, s, cus, &grid);
     if (e != hipSuccess)
         return e;
-    hipLaunchKernelGGL(argmax_final_kernel, dim3(batch), dim3(256), 0, s, a.partials, grid,
-                       a.tokens, a.vocab, a.draft);
+    return launch_argmax_final(a.partials, grid, a.tokens, a.vocab, a.draft, batch, s);
+}
+
+hipError_t launch_argmax_final(const Partial *partials, int nparts, const uint32_t *tokens,
+                               int vocab, uint32_t *draft, int batch, hipStream_t s)
+{
+    hipLaunchKernelGGL(argmax_final_kernel, dim3(batch), dim3(256), 0, s, partials, nparts,
+                       tokens, vocab, draft);
     return hipGetLastError();
 }
 

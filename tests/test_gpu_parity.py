@@ -248,3 +248,40 @@ def test_batched_fp8():
     assert np.array_equal(q.cpu().numpy(), ref[0])
     _, _, reps = _check_all(cfg, wts, tokens, hidden, dw, (q, s), ref)
     _say(f"[batched fp8] max err {max(r.max_err for r in reps):.4g}")
+
+
+@pytest.mark.slow
+def test_neartie_bf16_and_fp8():
+    """Near-tie stress (H = 6144, V = 154880, B = 8, Student-t(3) hidden, 64
+    planted ids per sequence within 1e-3 of the max).  BF16 head: every planted
+    logit rounds to the same value, so the draft must be the lowest planted id.
+    FP8 head: the same where the quantised planted rows still round to one BF16
+    value; otherwise the near-max and self-consistency rules."""
+    from tests import neartie
+    cfg = synth.CONFIGS["neartie"]
+    _say("\n[neartie] generating weights and planting")
+    wts = synth.make_weights(cfg)
+    tokens, hidden = synth.make_inputs(cfg)
+    nt = neartie.build(cfg, wts, tokens, hidden)
+    neartie.verify(nt, wts, tokens, hidden)
+    w2 = dict(wts)
+    w2["lm_head"] = nt.lm_head
+    dw = harness.upload(w2)
+    d, lg = harness.run_draft(dw, tokens, hidden)
+    mins = [min(p) for p in nt.planted]
+    assert [int(v) for v in d] == mins
+    _, _, reps = _check_all(cfg, w2, tokens, hidden, dw)
+    q, s = harness.quantize_dev(dw)
+    ref = oracle.quantize_fp8(nt.lm_head)
+    assert np.array_equal(q.cpu().numpy(), ref[0])
+    assert np.array_equal(s.cpu().numpy(), ref[1])
+    d8, lg8, reps8 = _check_all(cfg, w2, tokens, hidden, dw, (q, s), ref)
+    exact_fp8 = 0
+    for b in range(cfg.batch):
+        r = oracle.draft(w2, int(tokens[b]), hidden[b], fp8=ref)
+        P = np.array(nt.planted[b])
+        if np.all(r["logits"][P] == r["logits"][P[0]]) and r["draft"] == P.min():
+            assert int(d8[b]) == P.min(), b
+            exact_fp8 += 1
+    _say(f"[neartie] BF16 drafts == lowest planted ids for all {cfg.batch}; "
+         f"FP8 exact-tie sequences: {exact_fp8}/{cfg.batch}")
