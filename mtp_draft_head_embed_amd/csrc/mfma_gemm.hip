@@ -16,14 +16,17 @@
 //     l/16; D lane l holds m = 4*(l/16) + i, n = l%16.  Both operands take
 //     the same columns for a given (lane group, element), so the order in
 //     which k is split over lanes does not change the sum's terms.
-//   * The activations of a K-chunk are staged in LDS ([16*NBT][KC + 8] BF16,
-//     rows padded by 16 B so the 16 lanes of a row group hit distinct banks);
-//     each wave owns up to MAXT 16-row weight tiles per pass and keeps their
-//     accumulators in registers across the chunks.
+//   * The activations of a K-chunk are staged in LDS once per workgroup
+//     ([B][KC + 8] BF16, rows padded by 16 B so the 16 lanes of a row group hit
+//     distinct banks; lanes of padded batch rows feed zeros instead).  With
+//     160 KiB of LDS a whole K = 6144 chunk fits up to B = 12.  Each wave owns
+//     an equal contiguous share of the weight rows, walks the 16-row tiles that
+//     cover it (MAXT per pass, accumulators kept across chunks) and loads only
+//     its own rows.
 //   * FP8 codes are decoded to BF16 in registers (v_cvt_scalef32_pk_bf16_fp8
 //     with scale 1, exact for every E4M3FN value); the per-row scale multiplies
 //     the FP32 sum once, as the FP8 head defines it.
-//   * Weights stream with 16-byte non-temporal loads, UK k-steps in flight.
+//   * Weights stream with 16-byte non-temporal loads, 16 KiB in flight per wave.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -60,33 +63,74 @@ __device__ __forceinline__ bf16x8 fp8x8_to_bf16(uint32_t lo, uint32_t hi)
     return r;
 }
 
-template <bool FP8, int EPI, int NBT, int MAXT, int UK>
-__global__ __launch_bounds__(256) void mfma_gemm_kernel(MfmaArgs a)
+template <bool FP8, int EPI, int NBT, int MAXT, int UK, int WPB, bool MULTI>
+__global__ __launch_bounds__(WPB * 64) void mfma_gemm_kernel(MfmaArgs a)
 {
     extern __shared__ uint4 lds_raw[];
     uint16_t *As = reinterpret_cast<uint16_t *>(lds_raw);
     constexpr int BP = 16 * NBT;  // padded batch rows
-    const int lane = threadIdx.x & (kWave - 1);
-    const int wid = threadIdx.x / kWave;
-    const int nl = lane & 15;  // row within a tile (weights) / batch row (activations)
+    constexpr int NT = WPB * kWave;
+    const int tid = threadIdx.x;
+    const int lane = tid & (kWave - 1);
+    const int wid = tid / kWave;
+    const int nl = lane & 15;  // weight row within a tile / batch row within a batch tile
     const int g = lane >> 4;   // k-slot group
     const int KC = a.KC;
-    const int rs = KC + 8;     // LDS row stride in BF16 elements
+    const int rs = KC + 8;     // LDS row stride in BF16 elements (16 B of padding)
     const int B = a.B;
     const int N = a.N;
     const int K = a.K;
     const int split = blockIdx.y;
     const int k_begin = split * a.Ks;
     const int k_end = min(K, k_begin + a.Ks);
-    const int T = (N + 15) / 16;
-    const int Wt = gridDim.x * 4;
-    const int gw = blockIdx.x * 4 + wid;
+    const int nchunks = (k_end - k_begin + KC - 1) / KC;
     const char *Wb = reinterpret_cast<const char *>(a.W);
     const size_t wrow = FP8 ? size_t(K) : size_t(K) * 2;  // bytes per weight row
 
-    // padded activation rows stay zero for the whole kernel
-    for (int i = threadIdx.x; i < (BP - B) * (rs / 8); i += blockDim.x)
-        *reinterpret_cast<uint4 *>(As + size_t(B) * rs + size_t(i) * 8) = make_uint4(0, 0, 0, 0);
+    // Each wave owns a contiguous, equal share of the rows (balanced in bytes);
+    // its tiles are the 16-row blocks that overlap the share, and rows outside
+    // the share are neither loaded nor reported.
+    const int Wt = gridDim.x * WPB;
+    const int gw = blockIdx.x * WPB + wid;
+    const int T = (N + 15) / 16;
+    int R, r_lo, r_hi, t_lo, t_step, ntiles;
+    if (a.interleave) {
+        // tile t goes to wave t mod Wt: at any moment the grid streams one
+        // contiguous window of rows
+        R = ((T + Wt - 1) / Wt) * 16;
+        r_lo = 0;
+        r_hi = N;
+        t_lo = gw;
+        t_step = Wt;
+        ntiles = gw < T ? (T - gw + Wt - 1) / Wt : 0;
+    } else {
+        R = (N + Wt - 1) / Wt;
+        r_lo = min(N, gw * R);
+        r_hi = min(N, r_lo + R);
+        t_lo = r_lo / 16;
+        t_step = 1;
+        ntiles = r_hi > r_lo ? (r_hi + 15) / 16 - t_lo : 0;
+    }
+    // Passes of MAXT tiles whose accumulators live across the K-chunks; the
+    // same pass count in every wave of the workgroup, so the barriers match.
+    // With a single chunk (!MULTI) the tiles are simply walked one by one.
+    const int npass = MULTI ? ((R + 15) / 16 + 1 + MAXT - 1) / MAXT : ntiles;
+
+    auto stage = [&](int kc0) {
+        const int kc_len = min(KC, k_end - kc0);
+        for (int i = tid; i < B * (KC / 8); i += NT) {
+            const int bb = i / (KC / 8);
+            const int c = (i - bb * (KC / 8)) * 8;
+            uint4 v = make_uint4(0, 0, 0, 0);
+            if (c < kc_len)
+                v = *reinterpret_cast<const uint4 *>(a.A + size_t(bb) * K + kc0 + c);
+            *reinterpret_cast<uint4 *>(As + size_t(bb) * rs + c) = v;
+        }
+    };
+    if (!MULTI) {
+        stage(k_begin);
+        __syncthreads();
+    }
 
     float best_v[NBT][4];
     uint32_t best_i[NBT][4];
@@ -98,12 +142,7 @@ __global__ __launch_bounds__(256) void mfma_gemm_kernel(MfmaArgs a)
             best_i[bt][i] = 0xFFFFFFFFu;
         }
 
-    // tile groups: every wave of the workgroup runs the same number of passes
-    // (the workgroup's first wave has the most tiles) so the barriers match
-    const int first_w = blockIdx.x * 4;
-    const int tiles_w0 = first_w < T ? (T - first_w + Wt - 1) / Wt : 0;
-    const int npass = (tiles_w0 + MAXT - 1) / MAXT;
-
+#pragma unroll 1
     for (int pass = 0; pass < npass; ++pass) {
         f32x4 acc[MAXT][NBT];
 #pragma unroll
@@ -112,75 +151,60 @@ __global__ __launch_bounds__(256) void mfma_gemm_kernel(MfmaArgs a)
             for (int bt = 0; bt < NBT; ++bt)
                 acc[j][bt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-        for (int kc0 = k_begin; kc0 < k_end; kc0 += KC) {
-            const int kc_len = min(KC, k_end - kc0);  // a multiple of 16
-            __syncthreads();  // previous chunk's LDS reads are done
-            for (int i = threadIdx.x; i < B * (KC / 8); i += blockDim.x) {
-                const int bb = i / (KC / 8);
-                const int c = (i - bb * (KC / 8)) * 8;
-                uint4 v = make_uint4(0, 0, 0, 0);
-                if (c < kc_len)
-                    v = *reinterpret_cast<const uint4 *>(a.A + size_t(bb) * K + kc0 + c);
-                *reinterpret_cast<uint4 *>(As + size_t(bb) * rs + c) = v;
+        for (int ch = 0; ch < (MULTI ? nchunks : 1); ++ch) {
+            const int kc0 = k_begin + ch * KC;
+            if (MULTI) {
+                __syncthreads();  // the previous chunk's LDS reads are done
+                stage(kc0);
+                __syncthreads();
             }
-            __syncthreads();
-
+            const int kc_len = min(KC, k_end - kc0);  // a multiple of 16
             // k-steps of 32 columns.  FP8 loads cover a pair of steps (64
             // columns), so the FP8 count is a whole number of pairs; columns
             // past the chunk are zero in LDS and not loaded from HBM.
             const int nsteps = FP8 ? 2 * ((kc_len + 63) / 64) : (kc_len + 31) / 32;
 #pragma unroll
             for (int j = 0; j < MAXT; ++j) {
-                const int t = gw + (pass * MAXT + j) * Wt;
-                if (t >= T)
+                const int tix = MULTI ? pass * MAXT + j : pass;
+                if ((!MULTI && j > 0) || tix >= ntiles)
                     continue;  // uniform across the wave
-                const int row = t * 16 + nl;
-                const bool row_ok = row < N;
-                const char *wr = Wb + size_t(row_ok ? row : 0) * wrow;
+                const int row = (t_lo + tix * t_step) * 16 + nl;
+                const bool row_ok = row >= r_lo && row < r_hi;
+                const char *wr = Wb + size_t(row_ok ? row : r_lo) * wrow;
 #pragma unroll 1
                 for (int s0 = 0; s0 < nsteps; s0 += UK) {
-                    bf16x8 wf[UK];
-                    if (!FP8) {
-                        uint4 raw[UK];
+                    constexpr int NL = FP8 ? UK / 2 : UK;  // 16-byte loads per lane
+                    uint4 raw[NL];
 #pragma unroll
-                        for (int u = 0; u < UK; ++u) {
-                            const int col = kc0 + (s0 + u) * 32 + g * 8;
-                            raw[u] = make_uint4(0, 0, 0, 0);
-                            if (row_ok && s0 + u < nsteps && col < k_end)
-                                raw[u] = ld_nt16(wr + size_t(col) * 2);
-                        }
-#pragma unroll
-                        for (int u = 0; u < UK; ++u)
-                            wf[u] = as_bf16x8(raw[u]);
-                    } else {
-                        // step pair p = (s0 + u) / 2: lane group g reads codes
-                        // [64p + 16g, +16); the even step takes the first 8
-                        uint4 raw[UK / 2];
-#pragma unroll
-                        for (int u = 0; u < UK / 2; ++u) {
-                            const int col = kc0 + ((s0 >> 1) + u) * 64 + g * 16;
-                            raw[u] = make_uint4(0, 0, 0, 0);
-                            if (row_ok && s0 + 2 * u < nsteps && col < k_end)
-                                raw[u] = ld_nt16(wr + size_t(col));
-                        }
-#pragma unroll
-                        for (int u = 0; u < UK / 2; ++u) {
-                            wf[2 * u] = fp8x8_to_bf16(raw[u].x, raw[u].y);
-                            wf[2 * u + 1] = fp8x8_to_bf16(raw[u].z, raw[u].w);
-                        }
+                    for (int u = 0; u < NL; ++u) {
+                        // BF16: step s0+u, columns [32 s + 8 g, +8)
+                        // FP8:  step pair (s0/2 + u), codes [64 p + 16 g, +16);
+                        //       the even step of the pair takes the first 8
+                        const int col = FP8 ? kc0 + ((s0 >> 1) + u) * 64 + g * 16
+                                            : kc0 + (s0 + u) * 32 + g * 8;
+                        const bool ok = row_ok && (FP8 ? s0 + 2 * u : s0 + u) < nsteps && col < k_end;
+                        raw[u] = ok ? ld_nt16(wr + size_t(col) * (FP8 ? 1 : 2)) : make_uint4(0, 0, 0, 0);
                     }
 #pragma unroll
                     for (int u = 0; u < UK; ++u) {
                         if (s0 + u < nsteps) {
-                            // LDS column of this lane's 8 activations for step s0+u
+                            bf16x8 wf;
+                            if (FP8) {
+                                const uint4 &r = raw[u >> 1];
+                                wf = (u & 1) ? fp8x8_to_bf16(r.z, r.w) : fp8x8_to_bf16(r.x, r.y);
+                            } else {
+                                wf = as_bf16x8(raw[u]);
+                            }
                             const int lc = FP8 ? ((s0 + u) >> 1) * 64 + g * 16 + ((s0 + u) & 1) * 8
                                                : (s0 + u) * 32 + g * 8;
 #pragma unroll
                             for (int bt = 0; bt < NBT; ++bt) {
-                                const uint4 av = *reinterpret_cast<const uint4 *>(
-                                    As + size_t(bt * 16 + nl) * rs + lc);
+                                const int arow = bt * 16 + nl;
+                                const uint4 av = arow < B ? *reinterpret_cast<const uint4 *>(
+                                                                As + size_t(arow) * rs + lc)
+                                                          : make_uint4(0, 0, 0, 0);
                                 acc[j][bt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                                    as_bf16x8(av), wf[u], acc[j][bt], 0, 0, 0);
+                                    as_bf16x8(av), wf, acc[j][bt], 0, 0, 0);
                             }
                         }
                     }
@@ -191,11 +215,11 @@ __global__ __launch_bounds__(256) void mfma_gemm_kernel(MfmaArgs a)
         // ---- epilogue for this pass's tiles ----------------------------------
 #pragma unroll
         for (int j = 0; j < MAXT; ++j) {
-            const int t = gw + (pass * MAXT + j) * Wt;
-            if (t >= T)
+            const int tix = MULTI ? pass * MAXT + j : pass;
+            if ((!MULTI && j > 0) || tix >= ntiles)
                 continue;
-            const int row = t * 16 + nl;
-            if (row >= N)
+            const int row = (t_lo + tix * t_step) * 16 + nl;
+            if (row < r_lo || row >= r_hi)
                 continue;
             const float sc = (FP8 && EPI == EPI_ARGMAX) ? a.scale[row] : 1.0f;
 #pragma unroll
@@ -240,7 +264,7 @@ __global__ __launch_bounds__(256) void mfma_gemm_kernel(MfmaArgs a)
                 }
         __syncthreads();  // LDS is reused for the cross-wave reduction
         float *rv = reinterpret_cast<float *>(lds_raw);
-        uint32_t *ri = reinterpret_cast<uint32_t *>(rv + 4 * BP);
+        uint32_t *ri = reinterpret_cast<uint32_t *>(rv + WPB * BP);
         if (nl == 0) {
 #pragma unroll
             for (int bt = 0; bt < NBT; ++bt)
@@ -251,10 +275,10 @@ __global__ __launch_bounds__(256) void mfma_gemm_kernel(MfmaArgs a)
                 }
         }
         __syncthreads();
-        for (int bb = threadIdx.x; bb < B; bb += blockDim.x) {
+        for (int bb = tid; bb < B; bb += NT) {
             float bv = rv[bb];
             uint32_t bi = ri[bb];
-            for (int w = 1; w < 4; ++w)
+            for (int w = 1; w < WPB; ++w)
                 if (better(rv[w * BP + bb], ri[w * BP + bb], bv, bi)) {
                     bv = rv[w * BP + bb];
                     bi = ri[w * BP + bb];
@@ -268,28 +292,23 @@ __global__ __launch_bounds__(256) void mfma_gemm_kernel(MfmaArgs a)
 // Host side
 // ---------------------------------------------------------------------------
 
-static int g_lds_limit = 0;  // per-block LDS bytes the device allows (queried once)
-
+// Per-workgroup LDS bytes the current device allows (160 KiB on gfx950).
 static int lds_limit()
 {
-    if (g_lds_limit == 0) {
-        int dev = 0, v = 0;
-        if (hipGetDevice(&dev) == hipSuccess &&
-            hipDeviceGetAttribute(&v, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) == hipSuccess &&
-            v > 0)
-            g_lds_limit = v;
-        else
-            g_lds_limit = 65536;
-    }
-    return g_lds_limit;
+    int dev = 0, v = 0;
+    if (hipGetDevice(&dev) == hipSuccess &&
+        hipDeviceGetAttribute(&v, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) == hipSuccess &&
+        v > 0)
+        return v;
+    return 65536;
 }
 
-// Chunk width: the largest multiple of 64 whose [16*NBT][KC+8] BF16 tile fits
+// Chunk width: the largest multiple of 64 whose [B][KC + 8] BF16 tile fits
 // the LDS budget, then evened out over the chunks a split needs.
-static int chunk_cols(int nbt, int klen)
+static int chunk_cols(int B, int klen)
 {
-    const int budget = min(lds_limit(), 65536) - 1024;
-    int kc_max = (budget / (16 * nbt * 2) - 8) / 64 * 64;
+    const int budget = min(lds_limit(), 160 * 1024) - 4096;
+    int kc_max = (budget / (B * 2) - 8) / 64 * 64;
     if (kc_max < 64)
         kc_max = 64;
     const int nch = (klen + kc_max - 1) / kc_max;
@@ -297,39 +316,45 @@ static int chunk_cols(int nbt, int klen)
     return kc < 64 ? 64 : kc;
 }
 
-template <bool FP8, int EPI, int NBT>
+template <bool FP8, int EPI, int NBT, int WPB>
 static hipError_t launch_mfma_nbt(MfmaArgs a, int grid, int splits, hipStream_t s)
 {
-    constexpr int MAXT = NBT == 1 ? 8 : (NBT == 2 ? 4 : 2);
-    constexpr int UK = FP8 ? 16 : 8;
-    a.KC = chunk_cols(NBT, a.Ks);
-    size_t lds = size_t(16 * NBT) * size_t(a.KC + 8) * 2;
-    const size_t red = size_t(4 * 16 * NBT) * 8;
+    constexpr int MAXT = NBT == 1 ? 4 : (NBT == 2 ? 2 : 1);
+    constexpr int UK = FP8 ? 32 : 16;
+    a.KC = chunk_cols(a.B, a.Ks);
+    const bool multi = a.KC < a.Ks;
+    auto kern = multi ? mfma_gemm_kernel<FP8, EPI, NBT, MAXT, UK, WPB, true>
+                      : mfma_gemm_kernel<FP8, EPI, NBT, 1, UK, WPB, false>;
+    size_t lds = size_t(a.B) * size_t(a.KC + 8) * 2;
+    const size_t red = size_t(WPB * 16 * NBT) * 8;
     if (lds < red)
         lds = red;
-    hipLaunchKernelGGL((mfma_gemm_kernel<FP8, EPI, NBT, MAXT, UK>), dim3(grid, splits), dim3(256),
-                       lds, s, a);
+    if (lds > 65536)
+        (void)hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
+                                  hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
+    hipLaunchKernelGGL(kern, dim3(grid, splits), dim3(WPB * 64), lds, s, a);
     return hipGetLastError();
 }
 
-template <bool FP8, int EPI>
+template <bool FP8, int EPI, int WPB>
 static hipError_t launch_mfma(const MfmaArgs &a, int grid, int splits, hipStream_t s)
 {
-    const int nbt = (a.B + 15) / 16;
-    switch (nbt) {
-    case 1: return launch_mfma_nbt<FP8, EPI, 1>(a, grid, splits, s);
-    case 2: return launch_mfma_nbt<FP8, EPI, 2>(a, grid, splits, s);
-    case 3: return launch_mfma_nbt<FP8, EPI, 3>(a, grid, splits, s);
-    default: return launch_mfma_nbt<FP8, EPI, 4>(a, grid, splits, s);
+    switch ((a.B + 15) / 16) {
+    case 1: return launch_mfma_nbt<FP8, EPI, 1, WPB>(a, grid, splits, s);
+    case 2: return launch_mfma_nbt<FP8, EPI, 2, WPB>(a, grid, splits, s);
+    case 3: return launch_mfma_nbt<FP8, EPI, 3, WPB>(a, grid, splits, s);
+    default: return launch_mfma_nbt<FP8, EPI, 4, WPB>(a, grid, splits, s);
     }
 }
 
+// eh_proj (N = H rows, K = 2H) for B >= 2: one 16-row tile per wave, four
+// waves per workgroup, K split so that the grid is about 3 workgroups per CU.
 EhSplit eh_split(int hidden)
 {
-    // aim for about 2048 waves: one 16-row tile per wave, K split S ways
     const int T = (hidden + 15) / 16;
     const int K = 2 * hidden;
-    int S = (2048 + T - 1) / T;
+    const int wgs_per_split = (T + 3) / 4;
+    int S = (768 + wgs_per_split - 1) / wgs_per_split;
     if (S < 1)
         S = 1;
     if (S > 32)
@@ -350,16 +375,17 @@ hipError_t launch_eh_proj_mfma(const MfmaArgs &a_in, hipStream_t s)
     int grid = (T + 3) / 4;  // one tile per wave
     if (grid > kMaxHeadBlocks)
         grid = kMaxHeadBlocks;
-    return launch_mfma<false, EPI_STORE>(a, grid, sp.S, s);
+    return launch_mfma<false, EPI_STORE, 4>(a, grid, sp.S, s);
 }
 
+// lm_head for B >= 2: one 8-wave workgroup per CU sharing the staged
+// activations; each wave streams an equal contiguous share of the rows.
 hipError_t launch_head_mfma(const MfmaArgs &a_in, bool fp8, int *grid_out, hipStream_t s)
 {
     MfmaArgs a = a_in;
     a.Ks = a.K;
-    const int T = (a.N + 15) / 16;
-    int grid = device_cu_count() * 2;
-    const int need = (T + 3) / 4;
+    int grid = device_cu_count();
+    const int need = (a.N + 8 * 64 - 1) / (8 * 64);  // at least 64 rows per wave
     if (grid > need)
         grid = need;
     if (grid > kMaxHeadBlocks)
@@ -367,8 +393,8 @@ hipError_t launch_head_mfma(const MfmaArgs &a_in, bool fp8, int *grid_out, hipSt
     if (grid < 1)
         grid = 1;
     *grid_out = grid;
-    return fp8 ? launch_mfma<true, EPI_ARGMAX>(a, grid, 1, s)
-               : launch_mfma<false, EPI_ARGMAX>(a, grid, 1, s);
+    return fp8 ? launch_mfma<true, EPI_ARGMAX, 8>(a, grid, 1, s)
+               : launch_mfma<false, EPI_ARGMAX, 8>(a, grid, 1, s);
 }
 
 }  // namespace mtp
