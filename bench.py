@@ -40,7 +40,41 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=12.0,
                    help="approximate budget for the oracle baseline sample")
+    p.add_argument("--no-batched", action="store_true",
+                   help="skip the batched (B = 16 FP8, B = 8) timings")
+    p.add_argument("--calib-copy", action="store_true",
+                   help="also run a plain 1 GiB device-to-device copy three times "
+                        "(the known-size kernel that HBM counters are scaled by)")
     return p.parse_args()
+
+
+def kernel_source_hash() -> str:
+    """SHA-256 of the sources of the single-sequence head kernel."""
+    import hashlib
+    h = hashlib.sha256()
+    for f in ("row_gemv.hip", "common.hpp", "kernels.hpp"):
+        with open(os.path.join(ROOT, "mtp_draft_head_embed_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def committed_traffic(name: str):
+    """HBM bytes per launch of the BF16 head kernel from the committed counter
+    summary, or None when the summary is missing or the kernel changed since."""
+    path = os.path.join(ROOT, "profiles", name)
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    for line in open(path):
+        if ":" in line and line.strip().startswith("- "):
+            k, v = line.strip()[2:].split(":", 1)
+            vals[k.strip()] = v.strip().strip("`")
+    if vals.get("kernel_source_sha256") != kernel_source_hash():
+        return None
+    try:
+        return int(vals["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
 
 
 def head_bytes(H: int, V: int, B: int, fp8: bool) -> int:
@@ -141,6 +175,44 @@ def main():
         }
         print(f"[bench] {name}: {res[name]}", file=sys.stderr, flush=True)
 
+    batched = None
+    if not args.no_batched and args.config == "large":
+        batched = {}
+        for bname, bcfg, paths in (("B16", synth.CONFIGS["batched"], ("fp8",)),
+                                   ("B8", synth.CONFIGS["neartie"], ("bf16", "fp8"))):
+            btok, bhid = synth.make_inputs(bcfg)
+            Bb = bcfg.batch
+            btk = torch.from_numpy(btok.astype(np.uint32).view(np.int32)).to(dev)
+            bhd = harness.to_dev_bf16(bhid)
+            bdr = torch.empty(Bb, dtype=torch.int32, device=dev)
+            blg = torch.empty((Bb, V), dtype=torch.bfloat16, device=dev)
+            bws = mtp.new_workspace(H, V, Bb)
+            for path in paths:
+                def bsweep():
+                    if path == "fp8":
+                        mtp.mtp_draft_fp8w(dw.w, q, s, Bb, btk, bhd, bdr, blg, bws, stream)
+                    else:
+                        mtp.mtp_draft_bf16(dw.w, Bb, btk, bhd, bdr, blg, bws, stream)
+                g_s, w_s = timed(bsweep, args.steps, args.warmup)
+                per = g_s / args.steps
+                batched[f"{bname}_{path}"] = {
+                    "batch": Bb, "calls_per_s": round(args.steps / w_s, 2),
+                    "sequences_per_s": round(Bb * args.steps / w_s, 1),
+                    "ms_per_call": round(per * 1e3, 5),
+                    "sweep_GBps": round(sweep_bytes(H, V, Bb, path == "fp8") / per / 1e9, 1),
+                    # dense multiply-adds of the call (eh_proj + lm_head), as MFMA work
+                    "sweep_TFLOPs": round(2.0 * Bb * (V * H + 2 * H * H) / per / 1e12, 1),
+                }
+        print(f"[bench] batched: {batched}", file=sys.stderr, flush=True)
+
+    if args.calib_copy:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
     main_path = "bf16"
     r = res[main_path]
     hb = head_bytes(H, V, B, False)
@@ -150,10 +222,12 @@ def main():
         "peak": HBM_PEAK_GBPS,
         "unit": "GB/s",
         "frac": round(r["lm_head_GBps"] / HBM_PEAK_GBPS, 4),
-        "traffic": None,
+        "traffic": committed_traffic("lm_head_bf16_large_traffic.md"),
         "kernel": "row_gemv_kernel<BF16, head-norm prologue, argmax-partials epilogue>; the "
                   "timed mtp_head_bf16 call also runs the one-workgroup-per-sequence "
                   "argmax_final_kernel after it",
+        "traffic_source": "profiles/lm_head_bf16_large_traffic.md (null when the kernel "
+                          "sources changed since the counters were taken)",
         "algorithmic_bytes_per_launch": hb,
         "avg_launch_us": round(r["head_us"], 2),
     }
@@ -197,6 +271,7 @@ def main():
                         "head_us": round(v["head_us"], 2),
                         "sweeps_per_s": round(v["sweeps_per_s"], 2),
                         "ms_per_step": round(v["ms_per_step"], 5)} for k, v in res.items()},
+        "batched": batched,
         "roofline": roof,
         "cpu_baseline": cpu,
     }
