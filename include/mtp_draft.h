@@ -63,7 +63,7 @@ enum {
 
 #define MTP_DRAFT_INVALID 0xFFFFFFFFu /* draft[b] when tokens[b] >= vocab */
 #define MTP_MAX_HIDDEN 8192
-#define MTP_MAX_VOCAB 1073741824 /* 2^30 */
+#define MTP_MAX_VOCAB 16777216 /* 2^24 */
 #define MTP_MAX_BATCH 64
 
 /* The drafter's weights, all BF16 device arrays (glm5next_mtp_head.rs: the

@@ -18,7 +18,9 @@
 //     which k is split over lanes does not change the sum's terms.
 //   * The activations of a K-chunk are staged in LDS once per workgroup
 //     ([B][KC + 8] BF16, rows padded by 16 B so the 16 lanes of a row group hit
-//     distinct banks; lanes of padded batch rows feed zeros instead).  With
+//     distinct banks).  Lanes of padded batch rows (m >= B) read a staged row
+//     too: their output rows are never read, and MFMA output rows depend only
+//     on their own A row.  With
 //     160 KiB of LDS a whole K = 6144 chunk fits up to B = 12.  Each wave owns
 //     an equal contiguous share of the weight rows, walks the 16-row tiles that
 //     cover it (MAXT per pass, accumulators kept across chunks) and loads only
@@ -40,6 +42,14 @@ typedef unsigned int u32x4v __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ uint4 ld_nt16(const char *p)
 {
     const u32x4v v = __builtin_nontemporal_load(reinterpret_cast<const u32x4v *>(p));
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+// 16-byte buffer load with the non-temporal hint; offsets outside the
+// resource's range return zero.
+__device__ __forceinline__ uint4 ld_buf16(__amdgpu_buffer_rsrc_t r, int off)
+{
+    const u32x4v v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 2);
     return make_uint4(v.x, v.y, v.z, v.w);
 }
 
@@ -72,7 +82,9 @@ __global__ __launch_bounds__(WPB * 64) void mfma_gemm_kernel(MfmaArgs a)
     constexpr int NT = WPB * kWave;
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
-    const int wid = tid / kWave;
+    // the wave index is uniform across the wave; saying so keeps everything
+    // derived from it (row range, buffer resource) in scalar registers
+    const int wid = __builtin_amdgcn_readfirstlane(tid / kWave);
     const int nl = lane & 15;  // weight row within a tile / batch row within a batch tile
     const int g = lane >> 4;   // k-slot group
     const int KC = a.KC;
@@ -86,35 +98,28 @@ __global__ __launch_bounds__(WPB * 64) void mfma_gemm_kernel(MfmaArgs a)
     const int nchunks = (k_end - k_begin + KC - 1) / KC;
     const char *Wb = reinterpret_cast<const char *>(a.W);
     const size_t wrow = FP8 ? size_t(K) : size_t(K) * 2;  // bytes per weight row
+    constexpr int ESZ = FP8 ? 1 : 2;
+    // this wave's 2 KiB exchange scratch, after the staged activations
+    char *xs = reinterpret_cast<char *>(lds_raw) + a.xs_off + wid * 2048;
 
     // Each wave owns a contiguous, equal share of the rows (balanced in bytes);
     // its tiles are the 16-row blocks that overlap the share, and rows outside
     // the share are neither loaded nor reported.
     const int Wt = gridDim.x * WPB;
     const int gw = blockIdx.x * WPB + wid;
-    const int T = (N + 15) / 16;
-    int R, r_lo, r_hi, t_lo, t_step, ntiles;
-    if (a.interleave) {
-        // tile t goes to wave t mod Wt: at any moment the grid streams one
-        // contiguous window of rows
-        R = ((T + Wt - 1) / Wt) * 16;
-        r_lo = 0;
-        r_hi = N;
-        t_lo = gw;
-        t_step = Wt;
-        ntiles = gw < T ? (T - gw + Wt - 1) / Wt : 0;
-    } else {
-        R = (N + Wt - 1) / Wt;
-        r_lo = min(N, gw * R);
-        r_hi = min(N, r_lo + R);
-        t_lo = r_lo / 16;
-        t_step = 1;
-        ntiles = r_hi > r_lo ? (r_hi + 15) / 16 - t_lo : 0;
-    }
-    // Passes of MAXT tiles whose accumulators live across the K-chunks; the
-    // same pass count in every wave of the workgroup, so the barriers match.
-    // With a single chunk (!MULTI) the tiles are simply walked one by one.
-    const int npass = MULTI ? ((R + 15) / 16 + 1 + MAXT - 1) / MAXT : ntiles;
+    const int R = (N + Wt - 1) / Wt;
+    const int r_lo = min(N, gw * R);
+    const int r_hi = min(N, r_lo + R);
+    const int t_lo = r_lo / 16;
+    const int ntiles = r_hi > r_lo ? (r_hi + 15) / 16 - t_lo : 0;
+    // The wave's rows as a buffer resource: loads outside [r_lo, r_hi) return
+    // zero in hardware, so partial tiles need no per-lane predicates.
+    const __amdgpu_buffer_rsrc_t wrsrc = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<char *>(Wb) + size_t(r_lo) * wrow, 0, int(size_t(r_hi - r_lo) * wrow), 0x00020000);
+    // With several K-chunks (MULTI): passes of MAXT tiles whose accumulators
+    // live across the chunks; the same pass count in every wave of the
+    // workgroup, so the barriers match.
+    const int npass = ((R + 15) / 16 + 1 + MAXT - 1) / MAXT;
 
     auto stage = [&](int kc0) {
         const int kc_len = min(KC, k_end - kc0);
@@ -142,107 +147,163 @@ __global__ __launch_bounds__(WPB * 64) void mfma_gemm_kernel(MfmaArgs a)
             best_i[bt][i] = 0xFFFFFFFFu;
         }
 
-#pragma unroll 1
-    for (int pass = 0; pass < npass; ++pass) {
-        f32x4 acc[MAXT][NBT];
+    // One group = 16 loads per lane = 8 segments of 128 B per row of a 16-row
+    // tile (BF16: 16 k-steps; FP8: 16 step pairs).  Load 2j fetches tile rows
+    // 0-7, load 2j+1 rows 8-15 of segment j, 8 lanes x 16 B per row, so every
+    // load instruction reads whole 128-B lines.
+    constexpr int NL = 16;
+    static_assert((FP8 ? UK / 2 : UK) == NL, "one group = 8 segments");
+    auto load_group = [&](uint4 (&raw)[NL], int tile0, int s0, int kc0, int kc_len) {
+        const int seg0 = kc0 * ESZ + (FP8 ? (s0 >> 1) * 64 : s0 * 64);  // row byte offset
+        const int lim = (kc0 + kc_len) * ESZ;  // end of this chunk in the row
+        // byte offsets inside the wave's rows; rows below r_lo go negative,
+        // i.e. huge as unsigned, and rows at or past r_hi exceed the range
+        const int vo0 = (tile0 - r_lo + (lane >> 3)) * int(wrow) + seg0 + (lane & 7) * 16;
+        const int vo1 = vo0 + 8 * int(wrow);
+        if (seg0 + 1024 <= lim) {
 #pragma unroll
-        for (int j = 0; j < MAXT; ++j)
+            for (int u = 0; u < NL; ++u)
+                raw[u] = ld_buf16(wrsrc, ((u & 1) ? vo1 : vo0) + (u >> 1) * 128);
+        } else {
+            // last group of a chunk: columns past the chunk read as zero too
 #pragma unroll
-            for (int bt = 0; bt < NBT; ++bt)
-                acc[j][bt] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-        for (int ch = 0; ch < (MULTI ? nchunks : 1); ++ch) {
-            const int kc0 = k_begin + ch * KC;
-            if (MULTI) {
-                __syncthreads();  // the previous chunk's LDS reads are done
-                stage(kc0);
-                __syncthreads();
+            for (int u = 0; u < NL; ++u) {
+                const bool col_ok = seg0 + (u >> 1) * 128 + (lane & 7) * 16 < lim;
+                const int vo = ((u & 1) ? vo1 : vo0) + (u >> 1) * 128;
+                raw[u] = ld_buf16(wrsrc, col_ok ? vo : int(0x80000000u));
             }
-            const int kc_len = min(KC, k_end - kc0);  // a multiple of 16
-            // k-steps of 32 columns.  FP8 loads cover a pair of steps (64
-            // columns), so the FP8 count is a whole number of pairs; columns
-            // past the chunk are zero in LDS and not loaded from HBM.
-            const int nsteps = FP8 ? 2 * ((kc_len + 63) / 64) : (kc_len + 31) / 32;
+        }
+    };
+    // Re-lay each segment through this wave's LDS scratch into MFMA layout:
+    // lane (g, n) takes row n, 16-byte piece 4s + g for the segment's step
+    // (pair) s = 0, 1 -- the same columns as the activation reads.  Piece p of
+    // row r sits at slot p ^ ((r >> 1) & 7) so 16 lanes of a read hit distinct
+    // banks.  Then one MFMA per k-step and batch tile.
+    auto compute_group = [&](uint4 (&raw)[NL], f32x4 (&acc)[NBT], int s0, int nsteps) {
 #pragma unroll
-            for (int j = 0; j < MAXT; ++j) {
-                const int tix = MULTI ? pass * MAXT + j : pass;
-                if ((!MULTI && j > 0) || tix >= ntiles)
-                    continue;  // uniform across the wave
-                const int row = (t_lo + tix * t_step) * 16 + nl;
-                const bool row_ok = row >= r_lo && row < r_hi;
-                const char *wr = Wb + size_t(row_ok ? row : r_lo) * wrow;
-#pragma unroll 1
-                for (int s0 = 0; s0 < nsteps; s0 += UK) {
-                    constexpr int NL = FP8 ? UK / 2 : UK;  // 16-byte loads per lane
-                    uint4 raw[NL];
+        for (int j = 0; j < NL / 2; ++j) {
+            const int wr0 = lane >> 3, wp = lane & 7;
+            *reinterpret_cast<uint4 *>(xs + wr0 * 128 + ((wp ^ ((wr0 >> 1) & 7)) * 16)) = raw[2 * j];
+            const int wr1 = 8 + wr0;
+            *reinterpret_cast<uint4 *>(xs + wr1 * 128 + ((wp ^ ((wr1 >> 1) & 7)) * 16)) = raw[2 * j + 1];
+            raw[2 * j] = *reinterpret_cast<const uint4 *>(xs + nl * 128 + ((g ^ ((nl >> 1) & 7)) * 16));
+            raw[2 * j + 1] =
+                *reinterpret_cast<const uint4 *>(xs + nl * 128 + (((4 + g) ^ ((nl >> 1) & 7)) * 16));
+        }
 #pragma unroll
-                    for (int u = 0; u < NL; ++u) {
-                        // BF16: step s0+u, columns [32 s + 8 g, +8)
-                        // FP8:  step pair (s0/2 + u), codes [64 p + 16 g, +16);
-                        //       the even step of the pair takes the first 8
-                        const int col = FP8 ? kc0 + ((s0 >> 1) + u) * 64 + g * 16
-                                            : kc0 + (s0 + u) * 32 + g * 8;
-                        const bool ok = row_ok && (FP8 ? s0 + 2 * u : s0 + u) < nsteps && col < k_end;
-                        raw[u] = ok ? ld_nt16(wr + size_t(col) * (FP8 ? 1 : 2)) : make_uint4(0, 0, 0, 0);
-                    }
+        for (int u = 0; u < UK; ++u) {
+            if (s0 + u < nsteps) {
+                bf16x8 wf;
+                if (FP8) {
+                    const uint4 &r = raw[u >> 1];
+                    wf = (u & 1) ? fp8x8_to_bf16(r.z, r.w) : fp8x8_to_bf16(r.x, r.y);
+                } else {
+                    wf = as_bf16x8(raw[u]);
+                }
+                const int lc = FP8 ? ((s0 + u) >> 1) * 64 + g * 16 + ((s0 + u) & 1) * 8
+                                   : (s0 + u) * 32 + g * 8;
 #pragma unroll
-                    for (int u = 0; u < UK; ++u) {
-                        if (s0 + u < nsteps) {
-                            bf16x8 wf;
-                            if (FP8) {
-                                const uint4 &r = raw[u >> 1];
-                                wf = (u & 1) ? fp8x8_to_bf16(r.z, r.w) : fp8x8_to_bf16(r.x, r.y);
-                            } else {
-                                wf = as_bf16x8(raw[u]);
-                            }
-                            const int lc = FP8 ? ((s0 + u) >> 1) * 64 + g * 16 + ((s0 + u) & 1) * 8
-                                               : (s0 + u) * 32 + g * 8;
+                for (int bt = 0; bt < NBT; ++bt) {
+                    // padded batch rows only feed output rows that are dropped,
+                    // so they may read any staged row
+                    const int arow = min(bt * 16 + nl, B - 1);
+                    const uint4 av = *reinterpret_cast<const uint4 *>(As + size_t(arow) * rs + lc);
+                    acc[bt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(av), wf, acc[bt], 0, 0,
+                                                                      0);
+                }
+            }
+        }
+    };
+    // Rows of one finished tile: store / round, argmax bookkeeping.
+    auto epilogue = [&](f32x4 (&acc)[NBT], int tile0) {
+        const int row = tile0 + nl;
+        if (row < r_lo || row >= r_hi)
+            return;
+        const float sc = (FP8 && EPI == EPI_ARGMAX) ? a.scale[row] : 1.0f;
 #pragma unroll
-                            for (int bt = 0; bt < NBT; ++bt) {
-                                const int arow = bt * 16 + nl;
-                                const uint4 av = arow < B ? *reinterpret_cast<const uint4 *>(
-                                                                As + size_t(arow) * rs + lc)
-                                                          : make_uint4(0, 0, 0, 0);
-                                acc[j][bt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                                    as_bf16x8(av), wf, acc[j][bt], 0, 0, 0);
-                            }
-                        }
+        for (int bt = 0; bt < NBT; ++bt) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int bb = bt * 16 + g * 4 + i;
+                if (bb >= B)
+                    continue;
+                const float z = acc[bt][i];
+                if (EPI == EPI_STORE) {
+                    a.out_f32[(size_t(split) * B + bb) * N + row] = z;
+                } else {
+                    const uint32_t lb = f32_to_bf16_bits(FP8 ? z * sc : z);
+                    if (a.logits)
+                        a.logits[size_t(bb) * N + row] = uint16_t(lb);
+                    const float lv = __uint_as_float(lb << 16);
+                    if (better(lv, uint32_t(row), best_v[bt][i], best_i[bt][i])) {
+                        best_v[bt][i] = lv;
+                        best_i[bt][i] = uint32_t(row);
                     }
                 }
             }
         }
+    };
 
-        // ---- epilogue for this pass's tiles ----------------------------------
+    if (!MULTI) {
+        // One chunk holds all of K: walk the tiles one by one with a single
+        // accumulator.  (Double-buffering the groups in registers was measured:
+        // no gain for the head, and the extra registers cost the split-K
+        // eh_proj a workgroup per CU.)
+        const int kc_len = k_end - k_begin;
+        const int nsteps = FP8 ? 2 * ((kc_len + 63) / 64) : (kc_len + 31) / 32;
+#pragma unroll 1
+        for (int t = 0; t < ntiles; ++t) {
+            const int tile0 = (t_lo + t) * 16;
+            f32x4 acc[NBT];
 #pragma unroll
-        for (int j = 0; j < MAXT; ++j) {
-            const int tix = MULTI ? pass * MAXT + j : pass;
-            if ((!MULTI && j > 0) || tix >= ntiles)
-                continue;
-            const int row = (t_lo + tix * t_step) * 16 + nl;
-            if (row < r_lo || row >= r_hi)
-                continue;
-            const float sc = (FP8 && EPI == EPI_ARGMAX) ? a.scale[row] : 1.0f;
+            for (int bt = 0; bt < NBT; ++bt)
+                acc[bt] = f32x4{0.f, 0.f, 0.f, 0.f};
+            uint4 raw[NL];
+#pragma unroll 1
+            for (int s0 = 0; s0 < nsteps; s0 += UK) {
+                load_group(raw, tile0, s0, k_begin, kc_len);
+                compute_group(raw, acc, s0, nsteps);
+            }
+            epilogue(acc, tile0);
+        }
+    } else {
+#pragma unroll 1
+        for (int pass = 0; pass < npass; ++pass) {
+            f32x4 acc[MAXT][NBT];
 #pragma unroll
-            for (int bt = 0; bt < NBT; ++bt) {
+            for (int j = 0; j < MAXT; ++j)
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int bb = bt * 16 + g * 4 + i;
-                    if (bb >= B)
-                        continue;
-                    const float z = acc[j][bt][i];
-                    if (EPI == EPI_STORE) {
-                        a.out_f32[(size_t(split) * B + bb) * N + row] = z;
-                    } else {
-                        const uint32_t lb = f32_to_bf16_bits(FP8 ? z * sc : z);
-                        if (a.logits)
-                            a.logits[size_t(bb) * N + row] = uint16_t(lb);
-                        const float lv = __uint_as_float(lb << 16);
-                        if (better(lv, uint32_t(row), best_v[bt][i], best_i[bt][i])) {
-                            best_v[bt][i] = lv;
-                            best_i[bt][i] = uint32_t(row);
-                        }
+                for (int bt = 0; bt < NBT; ++bt)
+                    acc[j][bt] = f32x4{0.f, 0.f, 0.f, 0.f};
+            for (int ch = 0; ch < nchunks; ++ch) {
+                const int kc0 = k_begin + ch * KC;
+                __syncthreads();  // the previous chunk's LDS reads are done
+                stage(kc0);
+                __syncthreads();
+                const int kc_len = min(KC, k_end - kc0);  // a multiple of 16
+                // k-steps of 32 columns.  FP8 loads cover a pair of steps (64
+                // columns), so the FP8 count is a whole number of pairs; columns
+                // past the chunk are zero in LDS and not loaded from HBM.
+                const int nsteps = FP8 ? 2 * ((kc_len + 63) / 64) : (kc_len + 31) / 32;
+#pragma unroll
+                for (int j = 0; j < MAXT; ++j) {
+                    const int tix = pass * MAXT + j;
+                    if (tix >= ntiles)
+                        continue;  // uniform across the wave
+                    const int tile0 = (t_lo + tix) * 16;
+                    uint4 raw[NL];
+#pragma unroll 1
+                    for (int s0 = 0; s0 < nsteps; s0 += UK) {
+                        load_group(raw, tile0, s0, kc0, kc_len);
+                        compute_group(raw, acc[j], s0, nsteps);
                     }
                 }
+            }
+#pragma unroll
+            for (int j = 0; j < MAXT; ++j) {
+                const int tix = pass * MAXT + j;
+                if (tix < ntiles)
+                    epilogue(acc[j], (t_lo + tix) * 16);
             }
         }
     }
@@ -305,9 +366,9 @@ static int lds_limit()
 
 // Chunk width: the largest multiple of 64 whose [B][KC + 8] BF16 tile fits
 // the LDS budget, then evened out over the chunks a split needs.
-static int chunk_cols(int B, int klen)
+static int chunk_cols(int B, int klen, int wpb)
 {
-    const int budget = min(lds_limit(), 160 * 1024) - 4096;
+    const int budget = min(lds_limit(), 160 * 1024) - 2048 - wpb * 2048;
     int kc_max = (budget / (B * 2) - 8) / 64 * 64;
     if (kc_max < 64)
         kc_max = 64;
@@ -321,11 +382,12 @@ static hipError_t launch_mfma_nbt(MfmaArgs a, int grid, int splits, hipStream_t 
 {
     constexpr int MAXT = NBT == 1 ? 4 : (NBT == 2 ? 2 : 1);
     constexpr int UK = FP8 ? 32 : 16;
-    a.KC = chunk_cols(a.B, a.Ks);
+    a.KC = chunk_cols(a.B, a.Ks, WPB);
     const bool multi = a.KC < a.Ks;
     auto kern = multi ? mfma_gemm_kernel<FP8, EPI, NBT, MAXT, UK, WPB, true>
                       : mfma_gemm_kernel<FP8, EPI, NBT, 1, UK, WPB, false>;
-    size_t lds = size_t(a.B) * size_t(a.KC + 8) * 2;
+    a.xs_off = int(align256(size_t(a.B) * size_t(a.KC + 8) * 2));
+    size_t lds = size_t(a.xs_off) + size_t(WPB) * 2048;
     const size_t red = size_t(WPB * 16 * NBT) * 8;
     if (lds < red)
         lds = red;

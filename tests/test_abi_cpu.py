@@ -40,10 +40,10 @@ def test_workspace_bytes():
     assert mtp.mtp_workspace_bytes(6144, 154880, 1) > 6144 * 2
     assert mtp.mtp_workspace_bytes(6144, 154880, 16) > mtp.mtp_workspace_bytes(6144, 154880, 1)
     for bad in [(0, 10, 1), (8, 10, 1), (8208, 10, 1), (24, 10, 1), (16, 0, 1), (16, 10, 0),
-                (16, 10, 65), (16, 2 ** 30 + 1, 1)]:
+                (16, 10, 65), (16, 2 ** 24 + 1, 1)]:
         assert mtp.mtp_workspace_bytes(*bad) == 0, bad
     assert mtp.mtp_workspace_bytes(16, 1, 1) > 0
-    assert mtp.mtp_workspace_bytes(8192, 2 ** 30, 64) > 0
+    assert mtp.mtp_workspace_bytes(8192, 2 ** 24, 64) > 0
 
 
 def _fake_weights(H=64, V=100, eps=1e-6, **over):
