@@ -178,4 +178,126 @@ __device__ __forceinline__ void norm_to_lds(const uint4 (&v)[4], const uint16_t 
     }
 }
 
+// Two vanilla norms in one workgroup with one round trip: the two vectors and
+// their weights are loaded up front and both sums of squares share one block
+// reduction.  dst0[j] = BF16(x0_j w0_j / r0), dst1[j] = BF16(x1_j w1_j / r1);
+// a vector with valid == false is read as zeros.  (dst in LDS or global.)
+__device__ __forceinline__ void dual_norm(const uint16_t *__restrict__ x0, bool valid0,
+                                          const uint16_t *__restrict__ w0,
+                                          const uint16_t *__restrict__ x1,
+                                          const uint16_t *__restrict__ w1, int n, float eps,
+                                          uint16_t *dst0, uint16_t *dst1, float *red)
+{
+    const int tid = threadIdx.x;
+    uint4 a[4], b[4], wa[4], wb[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int j = (i * blockDim.x + tid) * 8;
+        const bool in = j < n;
+        a[i] = (in && valid0) ? *reinterpret_cast<const uint4 *>(x0 + j) : make_uint4(0, 0, 0, 0);
+        b[i] = in ? *reinterpret_cast<const uint4 *>(x1 + j) : make_uint4(0, 0, 0, 0);
+        wa[i] = in ? *reinterpret_cast<const uint4 *>(w0 + j) : make_uint4(0, 0, 0, 0);
+        wb[i] = in ? *reinterpret_cast<const uint4 *>(w1 + j) : make_uint4(0, 0, 0, 0);
+    }
+    float s0 = 0.f, s1 = 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const uint32_t pa[4] = {a[i].x, a[i].y, a[i].z, a[i].w};
+        const uint32_t pb[4] = {b[i].x, b[i].y, b[i].z, b[i].w};
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            s0 = fmaf(bf16_lo(pa[q]), bf16_lo(pa[q]), s0);
+            s0 = fmaf(bf16_hi(pa[q]), bf16_hi(pa[q]), s0);
+            s1 = fmaf(bf16_lo(pb[q]), bf16_lo(pb[q]), s1);
+            s1 = fmaf(bf16_hi(pb[q]), bf16_hi(pb[q]), s1);
+        }
+    }
+    s0 = wave_sum(s0);
+    s1 = wave_sum(s1);
+    const int nw = blockDim.x / kWave;
+    __syncthreads();
+    if ((tid & (kWave - 1)) == 0) {
+        red[tid / kWave] = s0;
+        red[16 + tid / kWave] = s1;
+    }
+    __syncthreads();
+    float t0 = 0.f, t1 = 0.f;
+    for (int w = 0; w < nw; ++w) {
+        t0 += red[w];
+        t1 += red[16 + w];
+    }
+    const float r0 = sqrtf(t0 / float(n) + eps);
+    const float r1 = sqrtf(t1 / float(n) + eps);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int j = (i * blockDim.x + tid) * 8;
+        if (j < n) {
+            const uint32_t pa[4] = {a[i].x, a[i].y, a[i].z, a[i].w};
+            const uint32_t pb[4] = {b[i].x, b[i].y, b[i].z, b[i].w};
+            const uint32_t qa[4] = {wa[i].x, wa[i].y, wa[i].z, wa[i].w};
+            const uint32_t qb[4] = {wb[i].x, wb[i].y, wb[i].z, wb[i].w};
+            uint32_t oa[4], ob[4];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                oa[q] = pack_bf16x2((bf16_lo(pa[q]) * bf16_lo(qa[q])) / r0,
+                                    (bf16_hi(pa[q]) * bf16_hi(qa[q])) / r0);
+                ob[q] = pack_bf16x2((bf16_lo(pb[q]) * bf16_lo(qb[q])) / r1,
+                                    (bf16_hi(pb[q]) * bf16_hi(qb[q])) / r1);
+            }
+            *reinterpret_cast<uint4 *>(dst0 + j) = make_uint4(oa[0], oa[1], oa[2], oa[3]);
+            *reinterpret_cast<uint4 *>(dst1 + j) = make_uint4(ob[0], ob[1], ob[2], ob[3]);
+        }
+    }
+}
+
+// One vanilla norm with the vector and its weight loaded together.
+__device__ __forceinline__ void single_norm(const uint16_t *__restrict__ x,
+                                            const uint16_t *__restrict__ w, int n, float eps,
+                                            uint16_t *dst, float *red)
+{
+    const int tid = threadIdx.x;
+    uint4 a[4], wa[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int j = (i * blockDim.x + tid) * 8;
+        const bool in = j < n;
+        a[i] = in ? *reinterpret_cast<const uint4 *>(x + j) : make_uint4(0, 0, 0, 0);
+        wa[i] = in ? *reinterpret_cast<const uint4 *>(w + j) : make_uint4(0, 0, 0, 0);
+    }
+    float s0 = 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const uint32_t pa[4] = {a[i].x, a[i].y, a[i].z, a[i].w};
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            s0 = fmaf(bf16_lo(pa[q]), bf16_lo(pa[q]), s0);
+            s0 = fmaf(bf16_hi(pa[q]), bf16_hi(pa[q]), s0);
+        }
+    }
+    s0 = wave_sum(s0);
+    const int nw = blockDim.x / kWave;
+    __syncthreads();
+    if ((tid & (kWave - 1)) == 0)
+        red[tid / kWave] = s0;
+    __syncthreads();
+    float t0 = 0.f;
+    for (int w2 = 0; w2 < nw; ++w2)
+        t0 += red[w2];
+    const float r0 = sqrtf(t0 / float(n) + eps);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int j = (i * blockDim.x + tid) * 8;
+        if (j < n) {
+            const uint32_t pa[4] = {a[i].x, a[i].y, a[i].z, a[i].w};
+            const uint32_t qa[4] = {wa[i].x, wa[i].y, wa[i].z, wa[i].w};
+            uint32_t oa[4];
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                oa[q] = pack_bf16x2((bf16_lo(pa[q]) * bf16_lo(qa[q])) / r0,
+                                    (bf16_hi(pa[q]) * bf16_hi(qa[q])) / r0);
+            *reinterpret_cast<uint4 *>(dst + j) = make_uint4(oa[0], oa[1], oa[2], oa[3]);
+        }
+    }
+}
+
 }  // namespace mtp

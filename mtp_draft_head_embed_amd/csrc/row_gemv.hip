@@ -80,7 +80,7 @@ template <bool FP8, int PRO, int EPI, int RPI, int U, bool NT = true, int BS = 2
 __global__ __launch_bounds__(BS) void row_gemv_kernel(RowGemvArgs a)
 {
     extern __shared__ uint4 lds_raw[];
-    __shared__ float red[16];
+    __shared__ float red[32];
     __shared__ float best_v_s[16];
     __shared__ uint32_t best_i_s[16];
     uint16_t *act = reinterpret_cast<uint16_t *>(lds_raw);
@@ -135,16 +135,11 @@ __global__ __launch_bounds__(BS) void row_gemv_kernel(RowGemvArgs a)
         const uint32_t tok = a.tokens[b];
         const bool tok_ok = tok < uint32_t(a.vocab);
         const uint16_t *erow = a.embed + (tok_ok ? size_t(tok) * size_t(H) : 0);
-        uint4 v[4];
-        float ss = block_sumsq(erow, H, tok_ok, v, red);
-        norm_to_lds(v, a.enorm_w, H, sqrtf(ss / float(H) + a.eps), act);
-        ss = block_sumsq(a.hidden + size_t(b) * H, H, true, v, red);
-        norm_to_lds(v, a.hnorm_w, H, sqrtf(ss / float(H) + a.eps), act + H);
+        dual_norm(erow, tok_ok, a.enorm_w, a.hidden + size_t(b) * H, a.hnorm_w, H, a.eps, act,
+                  act + H, red);
     } else {
         // K = H: shared_head.norm(x[b])
-        uint4 v[4];
-        const float ss = block_sumsq(a.xin + size_t(b) * K, K, true, v, red);
-        norm_to_lds(v, a.norm_w, K, sqrtf(ss / float(K) + a.eps), act);
+        single_norm(a.xin + size_t(b) * K, a.norm_w, K, a.eps, act, red);
     }
     __syncthreads();
 
@@ -241,6 +236,8 @@ __global__ __launch_bounds__(256) void argmax_final_kernel(const Partial *__rest
     __shared__ uint32_t si[4];
     const int b = blockIdx.x;
     const int tid = threadIdx.x;
+    // the token check's load goes out together with the partials' loads
+    const bool invalid = tokens && tid == 0 && tokens[b] >= uint32_t(vocab);
     float bv = -INFINITY;
     uint32_t bi = 0xFFFFFFFFu;
     for (int p = tid; p < nparts; p += blockDim.x) {
@@ -263,7 +260,7 @@ __global__ __launch_bounds__(256) void argmax_final_kernel(const Partial *__rest
                 bv = sv[w];
                 bi = si[w];
             }
-        if (tokens && tokens[b] >= uint32_t(vocab))
+        if (invalid)
             bi = 0xFFFFFFFFu;
         draft[b] = bi;
     }
