@@ -42,6 +42,8 @@ def parse():
                    help="approximate budget for the oracle baseline sample")
     p.add_argument("--no-batched", action="store_true",
                    help="skip the batched (B = 16 FP8, B = 8) timings")
+    p.add_argument("--no-agreement", action="store_true",
+                   help="skip the BF16-vs-FP8 draft agreement study")
     p.add_argument("--calib-copy", action="store_true",
                    help="also run a plain 1 GiB device-to-device copy three times "
                         "(the known-size kernel that HBM counters are scaled by)")
@@ -205,6 +207,34 @@ def main():
                 }
         print(f"[bench] batched: {batched}", file=sys.stderr, flush=True)
 
+    agreement = None
+    if not args.no_agreement:
+        # How often the FP8 drafting copy proposes the same token as the BF16
+        # head (the page's reason for the copy: it may change acceptance, never
+        # an emitted token).  Random-init weights: a synthetic proxy only.
+        acfg = synth.custom(H, V, 64, 2001)
+        atok, ahid = synth.make_inputs(acfg)
+        Ba = acfg.batch
+        atk = torch.from_numpy(atok.astype(np.uint32).view(np.int32)).to(dev)
+        ahd = harness.to_dev_bf16(ahid)
+        adr16 = torch.empty(Ba, dtype=torch.int32, device=dev)
+        adr8 = torch.empty(Ba, dtype=torch.int32, device=dev)
+        alg16 = torch.empty((Ba, V), dtype=torch.bfloat16, device=dev)
+        aws = mtp.new_workspace(H, V, Ba)
+        mtp.mtp_draft_bf16(dw.w, Ba, atk, ahd, adr16, alg16, aws, stream)
+        mtp.mtp_draft_fp8w(dw.w, q, s, Ba, atk, ahd, adr8, None, aws, stream)
+        torch.cuda.synchronize()
+        d16 = adr16.cpu().numpy()
+        d8 = adr8.cpu().numpy()
+        lg16 = alg16.float()
+        top2 = torch.topk(lg16, 2, dim=1).values.cpu().numpy()
+        gaps = top2[:, 0] - top2[:, 1]
+        agree = int((d16 == d8).sum())
+        agreement = {"sequences": Ba, "agree": agree, "rate": round(agree / Ba, 4),
+                     "median_bf16_top2_gap": round(float(np.median(gaps)), 4),
+                     "data": "synthetic random-init weights (a proxy, not an acceptance rate)"}
+        print(f"[bench] agreement: {agreement}", file=sys.stderr, flush=True)
+
     if args.calib_copy:
         src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
         dst = torch.empty_like(src)
@@ -272,6 +302,7 @@ def main():
                         "sweeps_per_s": round(v["sweeps_per_s"], 2),
                         "ms_per_step": round(v["ms_per_step"], 5)} for k, v in res.items()},
         "batched": batched,
+        "draft_agreement_fp8_vs_bf16": agreement,
         "roofline": roof,
         "cpu_baseline": cpu,
     }

@@ -285,3 +285,87 @@ def test_neartie_bf16_and_fp8():
             exact_fp8 += 1
     _say(f"[neartie] BF16 drafts == lowest planted ids for all {cfg.batch}; "
          f"FP8 exact-tie sequences: {exact_fp8}/{cfg.batch}")
+
+
+@pytest.mark.parametrize("B", [1, 3])
+def test_graph_capture_replay(B):
+    """A captured draft call replays correctly: new inputs copied into the
+    captured buffers between replays (with eager work and synchronisation in
+    between), every replay checked against an eager call on its own buffers
+    and, for one replay, against the oracle."""
+    import mtp_draft_head_embed_amd as mtp
+    _say(f"\n[graph] B={B}")
+    H, V = 1024, 20000
+    cfg = synth.custom(H, V, B, 60 + B)
+    wts = synth.make_weights(cfg)
+    dw = harness.upload(wts)
+    q, s = harness.quantize_dev(dw)
+    tk = torch.zeros(B, dtype=torch.int32, device="cuda")
+    hd = torch.zeros((B, H), dtype=torch.bfloat16, device="cuda")
+    ws = mtp.new_workspace(H, V, B)
+    outs = {}
+    graphs = {}
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    for path in ("bf16", "fp8"):
+        dr = torch.empty(B, dtype=torch.int32, device="cuda")
+        lg = torch.empty((B, V), dtype=torch.bfloat16, device="cuda")
+        outs[path] = (dr, lg)
+        with torch.cuda.stream(side):  # warm-up outside the capture
+            if path == "fp8":
+                mtp.mtp_draft_fp8w(dw.w, q, s, B, tk, hd, dr, lg, ws)
+            else:
+                mtp.mtp_draft_bf16(dw.w, B, tk, hd, dr, lg, ws)
+        torch.cuda.current_stream().wait_stream(side)
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            if path == "fp8":
+                mtp.mtp_draft_fp8w(dw.w, q, s, B, tk, hd, dr, lg, ws)
+            else:
+                mtp.mtp_draft_bf16(dw.w, B, tk, hd, dr, lg, ws)
+        graphs[path] = g
+    torch.cuda.synchronize()
+    for trial in range(3):
+        tcfg = synth.custom(H, V, B, 600 + 10 * B + trial)
+        tokens, hidden = synth.make_inputs(tcfg)
+        tk.copy_(torch.from_numpy(tokens.view(np.int32)))
+        hd.copy_(harness.to_dev_bf16(hidden))
+        _ = (hd.float() * 2).sum()  # unrelated eager work between replays
+        torch.cuda.synchronize()
+        for path in ("bf16", "fp8"):
+            graphs[path].replay()
+            torch.cuda.synchronize()
+            d_g = outs[path][0].cpu().numpy().view(np.uint32).copy()
+            l_g = harness.bf16_bits(outs[path][1])
+            d_e, l_e = harness.run_draft(dw, tokens, hidden, fp8=(q, s) if path == "fp8" else None)
+            assert np.array_equal(d_g, d_e), (trial, path)
+            assert np.array_equal(l_g, l_e), (trial, path)
+            if trial == 1:
+                ref = oracle.quantize_fp8(wts["lm_head"]) if path == "fp8" else None
+                for b in range(B):
+                    r = oracle.draft(wts, int(tokens[b]), hidden[b], fp8=ref)
+                    rep = harness.compare_sequence(b, r["o"], l_g[b], int(d_g[b]), r["draft"],
+                                                   harness.TOL_FP8 if ref else harness.TOL_BF16)
+                    assert rep.ok, rep
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("B", [1, 2])
+def test_max_vocab(B):
+    """The largest vocabulary the ABI accepts (2^24 rows) at the smallest
+    hidden size: the longest per-wave row ranges on both kernel families."""
+    import mtp_draft_head_embed_amd as mtp
+    V, H = 1 << 24, 16
+    assert mtp.mtp_workspace_bytes(H, V, B) > 0 and mtp.mtp_workspace_bytes(H, V + 1, B) == 0
+    _say(f"\n[max vocab] V={V} H={H} B={B}")
+    cfg = synth.custom(H, V, B, 70 + B)
+    wts = synth.make_weights(cfg)
+    tokens, hidden = synth.make_inputs(cfg)
+    tokens[-1] = V - 1  # the last embedding row
+    dw = harness.upload(wts)
+    _check_all(cfg, wts, tokens, hidden, dw)
+    q, s = harness.quantize_dev(dw)
+    ref = oracle.quantize_fp8(wts["lm_head"])
+    assert np.array_equal(q.cpu().numpy(), ref[0])
+    assert np.array_equal(s.cpu().numpy(), ref[1])
+    _check_all(cfg, wts, tokens, hidden, dw, (q, s), ref)
