@@ -29,6 +29,7 @@ if ROOT not in sys.path:
 
 METRIC = "draft sweeps/sec and lm_head achieved HBM GB/s (% of peak), BF16 vs FP8"
 HBM_PEAK_GBPS = 8000.0
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # dense BF16 matrix-core peak (no sparsity)
 
 
 def parse():
@@ -42,6 +43,8 @@ def parse():
                    help="approximate budget for the oracle baseline sample")
     p.add_argument("--no-batched", action="store_true",
                    help="skip the batched (B = 16 FP8, B = 8) timings")
+    p.add_argument("--no-context", action="store_true",
+                   help="skip the context-row (prompt / catch-up rows) timings")
     p.add_argument("--no-agreement", action="store_true",
                    help="skip the BF16-vs-FP8 draft agreement study")
     p.add_argument("--calib-copy", action="store_true",
@@ -207,6 +210,49 @@ def main():
                 }
         print(f"[bench] batched: {batched}", file=sys.stderr, flush=True)
 
+    context = None
+    if not args.no_context and args.config == "large":
+        # Context rows through the front half (embed gather, dual norm, eh_proj
+        # as a GEMM over T rows), at the drafter's Large shape.
+        Tmax = 4096
+        ccfg = synth.custom(H, V, Tmax + 1, 2002)
+        ctok, chid = synth.make_inputs(ccfg)
+        ctk = torch.from_numpy(ctok.astype(np.uint32).view(np.int32)).to(dev)
+        chd = harness.to_dev_bf16(chid[:Tmax])
+        cx = torch.empty((Tmax, H), dtype=torch.bfloat16, device=dev)
+        cws = torch.empty(mtp.mtp_context_workspace_bytes(H, Tmax), dtype=torch.uint8,
+                          device=dev)
+        # three copies of eh_proj (3 x 151 MB, more than the 256 MB last-level
+        # cache), used in turn, so that every call streams it from HBM
+        t = dw.tensors
+        cw = [dw.w] + [mtp.mtp_weights(t["embed"], t["enorm_w"], t["hnorm_w"], t["head_norm_w"],
+                                       t["eh_proj"].clone(), t["lm_head"], float(wts["rms_eps"]))
+                       for _ in range(2)]
+        turn = [0]
+
+        def ctx_call(T):
+            turn[0] = (turn[0] + 1) % len(cw)
+            mtp.mtp_context_rows(cw[turn[0]], T, ctk, chd, cx, cws, stream)
+
+        context = {"eh_proj_copies": len(cw)}
+        for T in (4, 16, 128, 1024, 4096):
+            n = max(10, min(args.steps, 100 if T <= 128 else 20))
+            g_s, _ = timed(lambda: ctx_call(T), n, max(2, min(args.warmup, 5)))
+            per = g_s / n
+            flops = 2.0 * T * H * 2 * H
+            # eh_proj once, per row an embedding row, a hidden row, an x row and a
+            # token, plus the two norm weights
+            nbytes = H * (2 * H) * 2 + T * (H * 2 + H * 2 + H * 2 + 4) + 2 * H * 2
+            t_roof = max(flops / (MFMA_BF16_PEAK_TFLOPS * 1e12), nbytes / (HBM_PEAK_GBPS * 1e9))
+            context[f"T{T}"] = {
+                "us_per_call": round(per * 1e6, 2), "rows_per_s": round(T / per, 1),
+                "TFLOPs": round(flops / per / 1e12, 1), "GBps": round(nbytes / per / 1e9, 1),
+                "bound": "mfma" if flops / (MFMA_BF16_PEAK_TFLOPS * 1e12) > nbytes / (
+                    HBM_PEAK_GBPS * 1e9) else "hbm",
+                "roofline_frac": round(t_roof / per, 3),
+            }
+        print(f"[bench] context rows: {context}", file=sys.stderr, flush=True)
+
     agreement = None
     if not args.no_agreement:
         # How often the FP8 drafting copy proposes the same token as the BF16
@@ -302,6 +348,7 @@ def main():
                         "sweeps_per_s": round(v["sweeps_per_s"], 2),
                         "ms_per_step": round(v["ms_per_step"], 5)} for k, v in res.items()},
         "batched": batched,
+        "context_rows": context,
         "draft_agreement_fp8_vs_bf16": agreement,
         "roofline": roof,
         "cpu_baseline": cpu,

@@ -65,6 +65,7 @@ enum {
 #define MTP_MAX_HIDDEN 8192
 #define MTP_MAX_VOCAB 16777216 /* 2^24 */
 #define MTP_MAX_BATCH 64
+#define MTP_MAX_CONTEXT_ROWS 65536
 
 /* The drafter's weights, all BF16 device arrays (glm5next_mtp_head.rs: the
  * head owns `embed_tokens`, the target's `lm_head`, and the MTP module's
@@ -153,6 +154,24 @@ int mtp_head_bf16(const mtp_weights *w, int32_t batch, const void *x, uint32_t *
 int mtp_head_fp8w(const mtp_weights *w, const uint8_t *q, const float *scale, int32_t batch,
                   const void *x, uint32_t *draft, void *logits, void *workspace,
                   size_t ws_bytes, void *stream);
+
+/* Context rows (glm5next_mtp_head.rs, `rows_impl`): the drafter's prompt or
+ * catch-up rows through the front half.  Row r pairs the embedding of
+ * tokens[r + 1] with hiddens[r]:
+ *   x[r] = BF16(eh_proj . [enorm(embed[tokens[r+1]]) | hnorm(hiddens[r])])
+ * (the page then writes each row into the MTP block's KV cache, which is not
+ * part of this library).  At many rows this is a dense GEMM on MFMA.
+ *   rows       T, 1 <= T <= MTP_MAX_CONTEXT_ROWS
+ *   tokens     device u32  [T + 1]   (tokens[0] is not read)
+ *   hiddens    device BF16 [T][H]
+ *   x          device BF16 [T][H]    (written; row r unspecified when
+ *                                     tokens[r + 1] >= V)
+ *   workspace  device, >= mtp_context_workspace_bytes(H, T)
+ * Uses w->embed, enorm_w, hnorm_w, eh_proj.  Asynchronous. */
+size_t mtp_context_workspace_bytes(int32_t hidden, int32_t rows);
+int mtp_context_rows(const mtp_weights *w, int32_t rows, const uint32_t *tokens,
+                     const void *hiddens, void *x, void *workspace, size_t ws_bytes,
+                     void *stream);
 
 /* Static text for a status code. */
 const char *mtp_status_str(int status);

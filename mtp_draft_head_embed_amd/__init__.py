@@ -20,7 +20,8 @@ __all__ = [
     "MTP_ERR_NONFINITE", "MTP_ERR_HIP", "MTP_DRAFT_INVALID", "MtpError", "mtp_weights",
     "lib", "lib_path", "mtp_workspace_bytes", "mtp_validate_draft_args",
     "mtp_quantize_head_fp8", "mtp_draft_bf16", "mtp_draft_fp8w", "mtp_front", "mtp_head_bf16",
-    "mtp_head_fp8w", "mtp_status_str", "new_workspace",
+    "mtp_head_fp8w", "mtp_status_str", "new_workspace", "mtp_context_workspace_bytes",
+    "mtp_context_rows",
 ]
 
 MTP_OK, MTP_ERR_NULL, MTP_ERR_SHAPE, MTP_ERR_ALIGN = 0, 1, 2, 3
@@ -74,6 +75,8 @@ def lib():
             "mtp_head_bf16": ([W, i32, P, P, P, P, sz, P], ctypes.c_int),
             "mtp_head_fp8w": ([W, P, P, i32, P, P, P, P, sz, P], ctypes.c_int),
             "mtp_status_str": ([ctypes.c_int], ctypes.c_char_p),
+            "mtp_context_workspace_bytes": ([i32, i32], sz),
+            "mtp_context_rows": ([W, i32, P, P, P, P, sz, P], ctypes.c_int),
         }
         for name, (args, res) in sigs.items():
             f = getattr(L, name)
@@ -243,3 +246,22 @@ def mtp_head_fp8w(w: mtp_weights, q, scale, batch: int, x, draft, logits, worksp
                                _dev(logits, "logits", torch.bfloat16, batch * V, optional=True),
                                _dev(workspace, "workspace", torch.uint8, 1), workspace.numel(),
                                _stream(stream)), "mtp_head_fp8w")
+
+
+def mtp_context_workspace_bytes(hidden: int, rows: int) -> int:
+    return int(lib().mtp_context_workspace_bytes(hidden, rows))
+
+
+def mtp_context_rows(w: mtp_weights, rows: int, tokens, hiddens, x, workspace,
+                     stream=None) -> None:
+    """Enqueue the front half for T context rows: row r pairs the embedding of
+    tokens[r + 1] with hiddens[r].  tokens int32/uint32 [T + 1], hiddens BF16
+    [T][H], x BF16 [T][H] (written)."""
+    H = w.hidden
+    t = (_dev(tokens, "tokens", torch.int32, rows + 1) if tokens.dtype == torch.int32
+         else _dev(tokens, "tokens", torch.uint32, rows + 1))
+    _check(lib().mtp_context_rows(w.ref(), rows, t,
+                                  _dev(hiddens, "hiddens", torch.bfloat16, rows * H),
+                                  _dev(x, "x", torch.bfloat16, rows * H),
+                                  _dev(workspace, "workspace", torch.uint8, 1), workspace.numel(),
+                                  _stream(stream)), "mtp_context_rows")

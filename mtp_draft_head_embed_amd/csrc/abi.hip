@@ -327,6 +327,76 @@ int mtp_head_fp8w(const mtp_weights *w, const uint8_t *q, const float *scale, in
                     static_cast<hipStream_t>(stream));
 }
 
+size_t mtp_context_workspace_bytes(int32_t hidden, int32_t rows)
+{
+    if (check_shape(hidden, 1, 1) != MTP_OK || rows < 1 || rows > MTP_MAX_CONTEXT_ROWS)
+        return 0;
+    if (rows < kCtxGemmMinRows)
+        return ws_layout(hidden, rows).total;
+    const CtxSplit sp = ctx_split(rows, hidden, 2 * hidden);
+    const size_t th = size_t(rows) * size_t(hidden);
+    size_t total = align256(th * 4);  // concat [T][2H] BF16
+    if (sp.S > 1)
+        total += align256(size_t(sp.S) * th * 4);  // FP32 partials [S][T][H]
+    return total;
+}
+
+int mtp_context_rows(const mtp_weights *w, int32_t rows, const uint32_t *tokens,
+                     const void *hiddens, void *x, void *workspace, size_t ws_bytes, void *stream)
+{
+    if (!w)
+        return MTP_ERR_NULL;
+    MTP_TRY(check_shape(w->hidden, w->vocab, 1));
+    if (rows < 1 || rows > MTP_MAX_CONTEXT_ROWS)
+        return MTP_ERR_SHAPE;
+    MTP_TRY(check_ptrs({w->embed, w->enorm_w, w->hnorm_w, w->eh_proj, tokens, hiddens, x}));
+    if (!workspace)
+        return MTP_ERR_WORKSPACE;
+    if (!aligned16(workspace))
+        return MTP_ERR_ALIGN;
+    if (ws_bytes < mtp_context_workspace_bytes(w->hidden, rows))
+        return MTP_ERR_WORKSPACE;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const uint32_t *tok1 = tokens + 1;  // row r pairs tokens[r + 1] with hiddens[r]
+    if (rows == 1) {
+        if (launch_eh_proj(front_args(w, tok1, hiddens, x), 1, s) != hipSuccess)
+            return MTP_ERR_HIP;
+        return MTP_OK;
+    }
+    if (rows < kCtxGemmMinRows)
+        return run_front_batched(w, rows, tok1, hiddens, x, nullptr, workspace, s);
+    const int H = w->hidden;
+    FrontArgs f{};
+    f.embed = static_cast<const uint16_t *>(w->embed);
+    f.vocab = w->vocab;
+    f.H = H;
+    f.tokens = tok1;
+    f.hidden = static_cast<const uint16_t *>(hiddens);
+    f.enorm_w = static_cast<const uint16_t *>(w->enorm_w);
+    f.hnorm_w = static_cast<const uint16_t *>(w->hnorm_w);
+    f.eps = w->rms_eps;
+    f.concat = static_cast<uint16_t *>(workspace);
+    if (launch_front_concat(f, rows, s) != hipSuccess)
+        return MTP_ERR_HIP;
+    const CtxSplit sp = ctx_split(rows, H, 2 * H);
+    float *P = reinterpret_cast<float *>(
+        ws_at(workspace, align256(size_t(rows) * size_t(H) * 4)));
+    if (launch_ctx_gemm(f.concat, static_cast<const uint16_t *>(w->eh_proj),
+                        static_cast<uint16_t *>(x), P, rows, H, 2 * H, sp, s) != hipSuccess)
+        return MTP_ERR_HIP;
+    if (sp.S > 1) {
+        SumNormArgs r{};
+        r.P = P;
+        r.S = sp.S;
+        r.B = rows;
+        r.H = H;
+        r.x_out = static_cast<uint16_t *>(x);
+        if (launch_sum_norm(r, rows, s) != hipSuccess)
+            return MTP_ERR_HIP;
+    }
+    return MTP_OK;
+}
+
 const char *mtp_status_str(int status)
 {
     switch (status) {

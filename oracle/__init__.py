@@ -196,3 +196,26 @@ def draft(w: dict, token: int, hidden: np.ndarray, fp8: tuple | None = None,
     logits = bf16_from_f64(o)
     return {"concat": concat, "x_unrounded": x_un, "x": x, "xn": xn, "o": o,
             "logits": logits, "draft": argmax_bf16(logits)}
+
+
+def context_rows(w: dict, tokens: np.ndarray, hiddens: np.ndarray,
+                 nthreads: int | None = None) -> dict:
+    """Context rows (glm5next_mtp_head.rs, `rows_impl`): row r pairs the
+    embedding of tokens[r + 1] with hiddens[r] and runs enorm, hnorm, concat and
+    eh_proj.  Returns ``x`` as BF16 bits [T][H], ``x_unrounded`` (FP64) and the
+    BF16 ``concat`` rows [T][2H]; all zero in a row whose tokens[r + 1] is out
+    of range (the library leaves such a row unspecified)."""
+    T = hiddens.shape[0]
+    assert tokens.size == T + 1
+    H = w["embed"].shape[1]
+    x = np.zeros((T, H), dtype=np.uint16)
+    x_un = np.zeros((T, H), dtype=np.float64)
+    concat = np.zeros((T, 2 * H), dtype=np.uint16)
+    for r in range(T):
+        c = front(w["embed"], int(tokens[r + 1]), hiddens[r], w["enorm_w"], w["hnorm_w"],
+                  float(w["rms_eps"]))
+        if c is not None:
+            concat[r] = c
+            x_un[r] = gemv_bf16(w["eh_proj"], c, nthreads)
+            x[r] = bf16_from_f64(x_un[r])
+    return {"x": x, "x_unrounded": x_un, "concat": concat}

@@ -47,6 +47,43 @@ def bits_to_f64(b: np.ndarray) -> np.ndarray:
     return (np.asarray(b, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32).astype(np.float64)
 
 
+def check_eh_proj_rows(xg: np.ndarray, x_un: np.ndarray, concat: np.ndarray,
+                       eh_proj: np.ndarray) -> dict:
+    """Compare BF16 eh_proj outputs from the library (bits [T][H]) with the
+    oracle's unrounded FP64 values for the same rows.
+
+    Every element: |g - o| <= ulp(max(|g|, |o|)) / 2 + (K 2^-24 + 2^-12) m,
+    m = sum_k |W_ik c_k| over the oracle's concat c and K = 2H.  The first term
+    is the final BF16 rounding; K 2^-24 m bounds FP32 recursive summation of
+    the K exact BF16 x BF16 products; 2^-12 m covers the few concat entries
+    whose FP32 norm rounds to the neighbouring BF16 (each moves the sum by at
+    most 2^-7 |W_ik c_k|).  Near-total cancellation (|o| << m) makes a plain
+    ulp bound meaningless there, hence the m-scaled terms.  Then, over all
+    elements: >= 98% bit-equal to the oracle's BF16 x and >= 99.5% within one
+    ulp.  (One concat entry that rounds the other way shifts its whole row by
+    W_ik ulp(c_k), so a few rows can carry several one- and two-ulp moves; a
+    lost or doubled term moves most elements of every row by several ulps.)
+    Returns the statistics."""
+    g = bits_to_f64(xg)
+    o = np.asarray(x_un, dtype=np.float64)
+    K = concat.shape[-1]
+    m = np.abs(bits_to_f64(concat)) @ np.abs(bits_to_f64(eh_proj)).T
+    big = np.maximum(np.abs(g), np.abs(o))
+    e = np.floor(np.log2(np.maximum(big, 2.0 ** -133)))
+    ulp = 2.0 ** (np.maximum(e, -126.0) - 7)
+    bound = 0.5 * ulp + (K * 2.0 ** -24 + 2.0 ** -12) * m
+    err = np.abs(g - o)
+    worst = np.unravel_index(np.argmax(err / bound), err.shape)
+    assert np.all(err <= bound), (worst, err[worst], bound[worst], o[worst], m[worst])
+    from oracle import bf16_from_f64  # only the rounding of the oracle's own value
+    d = np.abs(bf16_order_key(xg) - bf16_order_key(bf16_from_f64(o)))
+    stats = {"elements": int(d.size), "not_equal": float(np.mean(d != 0)),
+             "over_1ulp": float(np.mean(d > 1)), "max_ulps": int(d.max())}
+    assert stats["not_equal"] < 0.02, stats
+    assert stats["over_1ulp"] < 0.005, stats
+    return stats
+
+
 @dataclasses.dataclass
 class DevWeights:
     w: mtp.mtp_weights

@@ -115,3 +115,10 @@ def test_binding_refuses_host_tensors():
     t = lambda *s: torch.zeros(*s, dtype=torch.bfloat16)
     with pytest.raises(ValueError):
         mtp.mtp_weights(t(V, H), t(H), t(H), t(H), t(H, 2 * H), t(V, H), 1e-6)
+
+
+def test_context_workspace_bytes():
+    assert mtp.mtp_context_workspace_bytes(6144, 1) > 0
+    assert mtp.mtp_context_workspace_bytes(6144, 4096) >= 4096 * 6144 * 4
+    for bad in [(6144, 0), (6144, 65537), (8, 10), (8208, 10)]:
+        assert mtp.mtp_context_workspace_bytes(*bad) == 0, bad

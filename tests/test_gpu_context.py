@@ -1,0 +1,63 @@
+"""GPU parity of the context-row front end (glm5next_mtp_head.rs, `rows_impl`:
+row r pairs the embedding of tokens[r + 1] with hiddens[r]) against the
+oracle's FP64 rows: each element within the final rounding plus the FP32
+summation bound (a plain one-ulp bound fails where the sum nearly cancels),
+almost all bit-equal (tests/harness.py, `check_eh_proj_rows`).  Covers the
+single-row kernel, the batched split-K sweep (2..16 rows) and the tiled MFMA
+GEMM (17+ rows, split over K for few tiles, with ragged row, column and K
+tiles)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from tests import harness
+
+pytestmark = pytest.mark.gpu
+
+
+def _run(H, V, T, seed, bad_row=None):
+    import mtp_draft_head_embed_amd as mtp
+    print(f"\n[context] H={H} V={V} T={T} seed={seed}", flush=True)
+    cfg = synth.custom(H, V, T + 1, seed)
+    wts = synth.make_weights(cfg)
+    tokens, hid = synth.make_inputs(cfg)        # T + 1 tokens and rows; use T rows
+    hiddens = np.ascontiguousarray(hid[:T])
+    if bad_row is not None:
+        tokens[bad_row + 1] = V + 5
+    dw = harness.upload(wts)
+    tk = torch.from_numpy(tokens.astype(np.uint32).view(np.int32)).cuda()
+    hd = harness.to_dev_bf16(hiddens)
+    x = torch.empty((T, H), dtype=torch.bfloat16, device="cuda")
+    ws = torch.empty(mtp.mtp_context_workspace_bytes(H, T), dtype=torch.uint8, device="cuda")
+    mtp.mtp_context_rows(dw.w, T, tk, hd, x, ws)
+    torch.cuda.synchronize()
+    xg = harness.bf16_bits(x)
+    ref = oracle.context_rows(wts, tokens, hiddens)
+    rows = [r for r in range(T) if r != bad_row]
+    st = harness.check_eh_proj_rows(xg[rows], ref["x_unrounded"][rows], ref["concat"][rows],
+                                    wts["eh_proj"])
+    print(f"[context] {st}", flush=True)
+    return xg
+
+
+@pytest.mark.parametrize("H,V,T,seed", [
+    (256, 3000, 1, 80), (256, 3000, 2, 81), (256, 3000, 16, 92), (256, 3000, 17, 93),
+    (256, 3000, 37, 82), (256, 3000, 64, 83),
+    (256, 3000, 65, 84), (256, 3000, 200, 85), (1040, 2000, 65, 86), (1040, 2000, 130, 87),
+    (512, 4000, 300, 88),
+])
+def test_context_rows(H, V, T, seed):
+    _run(H, V, T, seed)
+
+
+def test_context_rows_out_of_range_token():
+    """A row whose token is out of range leaves the other rows exact."""
+    _run(256, 3000, 100, 89, bad_row=41)
+    _run(256, 3000, 10, 90, bad_row=3)
+
+
+@pytest.mark.slow
+def test_context_rows_large_hidden():
+    _run(6144, 20000, 70, 91)
