@@ -6,6 +6,7 @@
 #include "../../include/mtp_draft.h"
 #include "common.hpp"
 #include "kernels.hpp"
+#include "ctx_gemm.hpp"
 
 using namespace mtp;
 

@@ -25,6 +25,7 @@
 
 #include "common.hpp"
 #include "kernels.hpp"
+#include "ctx_gemm.hpp"
 
 namespace mtp {
 

@@ -1,0 +1,22 @@
+// ctx_gemm.hpp -- launcher of the context-row eh_proj GEMM (ctx_gemm.hip).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mtp {
+
+// Context rows: C[M][N] = BF16(A[M][K] . W[N][K]^T) on MFMA, with K split S
+// ways (Ks columns each, a multiple of 128) when the tiles alone would leave
+// CUs idle; then the FP32 partials P[S][M][N] are summed by launch_sum_norm.
+struct CtxSplit {
+    int S, Ks;
+};
+CtxSplit ctx_split(int M, int N, int K);
+hipError_t launch_ctx_gemm(const uint16_t *A, const uint16_t *W, uint16_t *C, float *P, int M,
+                           int N, int K, CtxSplit sp, hipStream_t s);
+// Rows from which the context rows use the tiled GEMM instead of the batched
+// split-K sweep.
+constexpr int kCtxGemmMinRows = 17;
+
+}  // namespace mtp
