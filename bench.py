@@ -43,6 +43,8 @@ def parse():
                    help="approximate budget for the oracle baseline sample")
     p.add_argument("--no-batched", action="store_true",
                    help="skip the batched (B = 16 FP8, B = 8) timings")
+    p.add_argument("--no-chain", action="store_true",
+                   help="skip the chained-draft (K = 4 drafts per call) timings")
     p.add_argument("--no-context", action="store_true",
                    help="skip the context-row (prompt / catch-up rows) timings")
     p.add_argument("--no-agreement", action="store_true",
@@ -210,6 +212,26 @@ def main():
                 }
         print(f"[bench] batched: {batched}", file=sys.stderr, flush=True)
 
+    chain = None
+    if not args.no_chain:
+        # K chained drafts per call (each step takes the previous draft and
+        # block output), one sequence: the propose loop without host round trips.
+        K = 4
+        cdr = torch.empty((K, B), dtype=torch.int32, device=dev)
+        cws = torch.empty(mtp.mtp_chain_workspace_bytes(H, V, B), dtype=torch.uint8, device=dev)
+        chain = {"steps": K}
+        for name, fp8 in (("bf16", False), ("fp8", True)):
+            def ccall():
+                if fp8:
+                    mtp.mtp_draft_chain_fp8w(dw.w, q, s, K, B, tk, hd, cdr, None, cws, stream)
+                else:
+                    mtp.mtp_draft_chain_bf16(dw.w, K, B, tk, hd, cdr, None, cws, stream)
+            n = max(10, args.steps // K)
+            g_s, w_s = timed(ccall, n, max(2, args.warmup // K))
+            chain[name] = {"ms_per_call": round(g_s / n * 1e3, 4),
+                           "drafts_per_s": round(K * B * n / w_s, 1)}
+        print(f"[bench] chain: {chain}", file=sys.stderr, flush=True)
+
     context = None
     if not args.no_context and args.config == "large":
         # Context rows through the front half (embed gather, dual norm, eh_proj
@@ -348,6 +370,7 @@ def main():
                         "sweeps_per_s": round(v["sweeps_per_s"], 2),
                         "ms_per_step": round(v["ms_per_step"], 5)} for k, v in res.items()},
         "batched": batched,
+        "chained_drafts": chain,
         "context_rows": context,
         "draft_agreement_fp8_vs_bf16": agreement,
         "roofline": roof,

@@ -66,6 +66,7 @@ enum {
 #define MTP_MAX_VOCAB 16777216 /* 2^24 */
 #define MTP_MAX_BATCH 64
 #define MTP_MAX_CONTEXT_ROWS 65536
+#define MTP_MAX_CHAIN_STEPS 64
 
 /* The drafter's weights, all BF16 device arrays (glm5next_mtp_head.rs: the
  * head owns `embed_tokens`, the target's `lm_head`, and the MTP module's
@@ -172,6 +173,33 @@ size_t mtp_context_workspace_bytes(int32_t hidden, int32_t rows);
 int mtp_context_rows(const mtp_weights *w, int32_t rows, const uint32_t *tokens,
                      const void *hiddens, void *x, void *workspace, size_t ws_bytes,
                      void *stream);
+
+/* Chained drafts (glm5next_mtp_head.rs: `propose` writes several drafts per
+ * call -- the state's `last_drafted` -- each one a `forward_one`).  Step k + 1
+ * takes step k's draft as its token and step k's block output x as its hidden;
+ * the pages do not show which hidden the proposer feeds back, and with the
+ * block taken as the identity x is the MTP layer's output before
+ * shared_head.norm.  Equivalent to `steps` calls of mtp_draft_bf16 (or
+ * mtp_draft_fp8w) with those inputs, enqueued back to back with no host
+ * round trip.
+ *   steps      K, 1 <= K <= MTP_MAX_CHAIN_STEPS
+ *   tokens     device u32  [B]        first step's tokens
+ *   hidden     device BF16 [B][H]     first step's hidden
+ *   drafts     device u32  [K][B]     (written) drafts[k][b]; once a draft is
+ *                                      MTP_DRAFT_INVALID, every later one of
+ *                                      that sequence is too
+ *   logits     device BF16 [K][B][V]  (written) or NULL
+ *   workspace  device, >= mtp_chain_workspace_bytes(H, V, B)
+ * Other arguments and errors as for mtp_draft_bf16 / mtp_draft_fp8w; K out of
+ * range is MTP_ERR_SHAPE.  Asynchronous. */
+size_t mtp_chain_workspace_bytes(int32_t hidden, int32_t vocab, int32_t batch);
+int mtp_draft_chain_bf16(const mtp_weights *w, int32_t steps, int32_t batch,
+                         const uint32_t *tokens, const void *hidden, uint32_t *drafts,
+                         void *logits, void *workspace, size_t ws_bytes, void *stream);
+int mtp_draft_chain_fp8w(const mtp_weights *w, const uint8_t *q, const float *scale,
+                         int32_t steps, int32_t batch, const uint32_t *tokens, const void *hidden,
+                         uint32_t *drafts, void *logits, void *workspace, size_t ws_bytes,
+                         void *stream);
 
 /* Static text for a status code. */
 const char *mtp_status_str(int status);

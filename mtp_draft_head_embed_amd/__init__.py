@@ -77,6 +77,9 @@ def lib():
             "mtp_status_str": ([ctypes.c_int], ctypes.c_char_p),
             "mtp_context_workspace_bytes": ([i32, i32], sz),
             "mtp_context_rows": ([W, i32, P, P, P, P, sz, P], ctypes.c_int),
+            "mtp_chain_workspace_bytes": ([i32, i32, i32], sz),
+            "mtp_draft_chain_bf16": ([W, i32, i32, P, P, P, P, P, sz, P], ctypes.c_int),
+            "mtp_draft_chain_fp8w": ([W, P, P, i32, i32, P, P, P, P, P, sz, P], ctypes.c_int),
         }
         for name, (args, res) in sigs.items():
             f = getattr(L, name)
@@ -265,3 +268,43 @@ def mtp_context_rows(w: mtp_weights, rows: int, tokens, hiddens, x, workspace,
                                   _dev(x, "x", torch.bfloat16, rows * H),
                                   _dev(workspace, "workspace", torch.uint8, 1), workspace.numel(),
                                   _stream(stream)), "mtp_context_rows")
+
+
+def mtp_chain_workspace_bytes(hidden: int, vocab: int, batch: int) -> int:
+    return int(lib().mtp_chain_workspace_bytes(hidden, vocab, batch))
+
+
+def _chain_common(w, steps, batch, tokens, hidden, drafts, logits, workspace):
+    H, V = w.hidden, w.vocab
+    return (
+        _dev(tokens, "tokens", torch.int32, batch) if tokens.dtype == torch.int32
+        else _dev(tokens, "tokens", torch.uint32, batch),
+        _dev(hidden, "hidden", torch.bfloat16, batch * H),
+        _dev(drafts, "drafts", torch.int32, steps * batch) if drafts.dtype == torch.int32
+        else _dev(drafts, "drafts", torch.uint32, steps * batch),
+        _dev(logits, "logits", torch.bfloat16, steps * batch * V, optional=True),
+        _dev(workspace, "workspace", torch.uint8, 1), workspace.numel(),
+    )
+
+
+def mtp_draft_chain_bf16(w: mtp_weights, steps: int, batch: int, tokens, hidden, drafts, logits,
+                         workspace, stream=None) -> None:
+    """Enqueue `steps` chained drafts per sequence (BF16 lm_head): step k + 1
+    takes step k's draft and block output.  drafts int32/uint32 [K][B],
+    logits BF16 [K][B][V] or None."""
+    t, h, d, lg, ws, nws = _chain_common(w, steps, batch, tokens, hidden, drafts, logits,
+                                         workspace)
+    _check(lib().mtp_draft_chain_bf16(w.ref(), steps, batch, t, h, d, lg, ws, nws,
+                                      _stream(stream)), "mtp_draft_chain_bf16")
+
+
+def mtp_draft_chain_fp8w(w: mtp_weights, q, scale, steps: int, batch: int, tokens, hidden,
+                         drafts, logits, workspace, stream=None) -> None:
+    """As mtp_draft_chain_bf16 with the FP8 copy of lm_head (q, scale)."""
+    t, h, d, lg, ws, nws = _chain_common(w, steps, batch, tokens, hidden, drafts, logits,
+                                         workspace)
+    n = w.vocab * w.hidden
+    _check(lib().mtp_draft_chain_fp8w(w.ref(), _dev(q, "q", torch.uint8, n),
+                                      _dev(scale, "scale", torch.float32, w.vocab), steps, batch,
+                                      t, h, d, lg, ws, nws, _stream(stream)),
+           "mtp_draft_chain_fp8w")

@@ -220,14 +220,12 @@ int run_head(const mtp_weights *w, bool fp8, const uint8_t *q, const float *scal
     return MTP_OK;
 }
 
-int run_draft(const mtp_weights *w, bool fp8, const uint8_t *q, const float *scale,
-              int32_t batch, const uint32_t *tokens, const void *hidden, uint32_t *draft,
-              void *logits, void *ws, size_t ws_bytes, void *stream)
+// One whole sweep (arguments already validated), writing the block output to x.
+int run_sweep(const mtp_weights *w, bool fp8, const uint8_t *q, const float *scale,
+              int32_t batch, const uint32_t *tokens, const void *hidden, void *x,
+              uint32_t *draft, void *logits, void *ws, hipStream_t s)
 {
-    MTP_TRY(validate_draft(w, fp8, q, scale, batch, tokens, hidden, draft, logits, ws, ws_bytes));
-    hipStream_t s = static_cast<hipStream_t>(stream);
     const WsLayout L = ws_layout(w->hidden, batch);
-    void *x = ws_at(ws, L.x_off);
     if (batch > 1) {
         void *xn = ws_at(ws, L.xn_off);
         MTP_TRY(run_front_batched(w, batch, tokens, hidden, x, xn, ws, s));
@@ -236,6 +234,48 @@ int run_draft(const mtp_weights *w, bool fp8, const uint8_t *q, const float *sca
     if (launch_eh_proj(front_args(w, tokens, hidden, x), batch, s) != hipSuccess)
         return MTP_ERR_HIP;
     return run_head(w, fp8, q, scale, batch, x, tokens, draft, logits, ws, s);
+}
+
+int run_draft(const mtp_weights *w, bool fp8, const uint8_t *q, const float *scale,
+              int32_t batch, const uint32_t *tokens, const void *hidden, uint32_t *draft,
+              void *logits, void *ws, size_t ws_bytes, void *stream)
+{
+    MTP_TRY(validate_draft(w, fp8, q, scale, batch, tokens, hidden, draft, logits, ws, ws_bytes));
+    const WsLayout L = ws_layout(w->hidden, batch);
+    return run_sweep(w, fp8, q, scale, batch, tokens, hidden, ws_at(ws, L.x_off), draft, logits,
+                     ws, static_cast<hipStream_t>(stream));
+}
+
+// Chained drafts: workspace = the sweep's, then two block outputs used in turn.
+size_t chain_ws_bytes(int32_t hidden, int32_t batch)
+{
+    return ws_layout(hidden, batch).total + 2 * align256(size_t(batch) * size_t(hidden) * 2);
+}
+
+int run_chain(const mtp_weights *w, bool fp8, const uint8_t *q, const float *scale,
+              int32_t steps, int32_t batch, const uint32_t *tokens, const void *hidden,
+              uint32_t *drafts, void *logits, void *ws, size_t ws_bytes, void *stream)
+{
+    if (steps < 1 || steps > MTP_MAX_CHAIN_STEPS)
+        return MTP_ERR_SHAPE;
+    // the first step's arguments carry every check the later steps need
+    MTP_TRY(validate_draft(w, fp8, q, scale, batch, tokens, hidden, drafts, logits, ws, ws_bytes));
+    if (ws_bytes < chain_ws_bytes(w->hidden, batch))
+        return MTP_ERR_WORKSPACE;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const size_t base = ws_layout(w->hidden, batch).total;
+    void *xbuf[2] = {ws_at(ws, base),
+                     ws_at(ws, base + align256(size_t(batch) * size_t(w->hidden) * 2))};
+    const size_t lrow = size_t(batch) * size_t(w->vocab) * 2;  // logits bytes per step
+    for (int k = 0; k < steps; ++k) {
+        const uint32_t *tk = k == 0 ? tokens : drafts + size_t(k - 1) * batch;
+        const void *hd = k == 0 ? hidden : xbuf[(k - 1) & 1];
+        void *lg = logits ? static_cast<void *>(static_cast<char *>(logits) + size_t(k) * lrow)
+                          : nullptr;
+        MTP_TRY(run_sweep(w, fp8, q, scale, batch, tk, hd, xbuf[k & 1],
+                          drafts + size_t(k) * batch, lg, ws, s));
+    }
+    return MTP_OK;
 }
 
 }  // namespace
@@ -294,6 +334,30 @@ int mtp_draft_fp8w(const mtp_weights *w, const uint8_t *q, const float *scale, i
 {
     return run_draft(w, true, q, scale, batch, tokens, hidden, draft, logits, workspace, ws_bytes,
                      stream);
+}
+
+size_t mtp_chain_workspace_bytes(int32_t hidden, int32_t vocab, int32_t batch)
+{
+    if (check_shape(hidden, vocab, batch) != MTP_OK)
+        return 0;
+    return chain_ws_bytes(hidden, batch);
+}
+
+int mtp_draft_chain_bf16(const mtp_weights *w, int32_t steps, int32_t batch,
+                         const uint32_t *tokens, const void *hidden, uint32_t *drafts,
+                         void *logits, void *workspace, size_t ws_bytes, void *stream)
+{
+    return run_chain(w, false, nullptr, nullptr, steps, batch, tokens, hidden, drafts, logits,
+                     workspace, ws_bytes, stream);
+}
+
+int mtp_draft_chain_fp8w(const mtp_weights *w, const uint8_t *q, const float *scale,
+                         int32_t steps, int32_t batch, const uint32_t *tokens, const void *hidden,
+                         uint32_t *drafts, void *logits, void *workspace, size_t ws_bytes,
+                         void *stream)
+{
+    return run_chain(w, true, q, scale, steps, batch, tokens, hidden, drafts, logits, workspace,
+                     ws_bytes, stream);
 }
 
 int mtp_front(const mtp_weights *w, int32_t batch, const uint32_t *tokens, const void *hidden,

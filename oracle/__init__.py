@@ -219,3 +219,24 @@ def context_rows(w: dict, tokens: np.ndarray, hiddens: np.ndarray,
             x_un[r] = gemv_bf16(w["eh_proj"], c, nthreads)
             x[r] = bf16_from_f64(x_un[r])
     return {"x": x, "x_unrounded": x_un, "concat": concat}
+
+
+def draft_chain(w: dict, token: int, hidden: np.ndarray, steps: int, fp8: tuple | None = None,
+                nthreads: int | None = None) -> list:
+    """Chained drafts for one sequence: ``steps`` calls of ``draft``, step k + 1
+    taking step k's draft as its token and step k's block output x (BF16 bits)
+    as its hidden.  The pages show that a propose call writes several drafts
+    (glm5next_mtp_head.rs, the state's ``last_drafted``), each one
+    ``forward_one(token, hidden_in)``; which hidden is fed back is not shown,
+    and the block output is taken (the block being the identity).  Returns the
+    per-step results of ``draft``; a None entry (token out of range) ends the
+    chain, every later draft being invalid too."""
+    out = []
+    tok, hid = int(token), np.ascontiguousarray(hidden, dtype=np.uint16)
+    for _ in range(steps):
+        r = draft(w, tok, hid, fp8, nthreads)
+        out.append(r)
+        if r is None:
+            break
+        tok, hid = r["draft"], r["x"]
+    return out

@@ -122,3 +122,25 @@ def test_context_workspace_bytes():
     assert mtp.mtp_context_workspace_bytes(6144, 4096) >= 4096 * 6144 * 4
     for bad in [(6144, 0), (6144, 65537), (8, 10), (8208, 10)]:
         assert mtp.mtp_context_workspace_bytes(*bad) == 0, bad
+
+
+def test_chain_workspace_and_validation():
+    """Chained drafts: workspace = the sweep's plus two block outputs; a step
+    count out of range or a workspace sized for one sweep is refused before
+    anything is enqueued (fake device addresses are never touched)."""
+    H, V, B = 64, 100, 2
+    one = mtp.mtp_workspace_bytes(H, V, B)
+    ch = mtp.mtp_chain_workspace_bytes(H, V, B)
+    assert ch >= one + 2 * B * H * 2
+    assert mtp.mtp_chain_workspace_bytes(8, V, B) == 0
+    w = _fake_weights(H, V)
+    P = ctypes.c_void_p
+    args = lambda steps, nbytes: (ctypes.byref(w), steps, B, P(0x90000), P(0xA0000), P(0xB0000),
+                                  None, P(0xD0000), nbytes, None)
+    L = mtp.lib()
+    assert L.mtp_draft_chain_bf16(*args(0, ch)) == mtp.MTP_ERR_SHAPE
+    assert L.mtp_draft_chain_bf16(*args(65, ch)) == mtp.MTP_ERR_SHAPE
+    assert L.mtp_draft_chain_bf16(*args(3, one)) == mtp.MTP_ERR_WORKSPACE
+    assert L.mtp_draft_chain_fp8w(ctypes.byref(w), None, P(0x80000), 3, B, P(0x90000),
+                                  P(0xA0000), P(0xB0000), None, P(0xD0000), ch,
+                                  None) == mtp.MTP_ERR_NULL
