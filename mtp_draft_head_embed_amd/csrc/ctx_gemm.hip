@@ -6,21 +6,28 @@
 //
 // The page stops each row at the block's KV-cache write (out of scope here).
 // With T rows, eh_proj is a dense GEMM C[T][H] = A[T][2H] . W[H][2H]^T with
-// both operands K-contiguous; beyond a few hundred rows it is bound by the
-// matrix cores, so it is tiled for MFMA:
-//   * 128 x 128 output tile per 256-thread workgroup, four waves of 64 x 64,
-//     each a 4 x 4 grid of v_mfma_f32_16x16x32_bf16 accumulators;
-//   * K in steps of 64 through LDS, double-buffered: the next step's global
-//     loads (8 lanes x 16 B per row, whole 128-B lines) are in registers while
-//     the current step is multiplied, then written to the other buffer;
-//   * LDS rows padded to 72 BF16 (144 B) so the 16 lanes of a fragment read
-//     hit disjoint banks;
-//   * partial tiles (T or H not a multiple of 128, 2H not of 64) load zeros;
-//   * with few tiles (a skinny T) K is split over blockIdx.z so that about
-//     512 workgroups fill the 256 CUs; each split writes an FP32 partial tile
-//     and the splits are summed in split order by the batched path's
-//     sum-and-round kernel.
-// Sums are FP32 in a fixed k order, so results do not depend on timing.
+// both operands K-contiguous, HBM-bound for a few hundred rows and bound by
+// the matrix cores beyond.  One kernel, two tile shapes:
+//   * 256 x 256 output tile per 16-wave workgroup (one per CU) for many rows,
+//     128 x 128 per 8-wave workgroup (two per CU) for few; every wave owns a
+//     64 x 64 or 64 x 32 block of v_mfma_f32_16x16x32_bf16 accumulators;
+//   * K in steps of 32 columns through four LDS stages, each its own LDS
+//     object; the operands go from HBM straight into LDS (buffer loads with
+//     the LDS flag: no registers, no LDS store instructions), issued three
+//     steps ahead, so a step waits only for the loads of the step after it;
+//   * a staged row is 64 bytes; 16-byte piece c of row r sits at slot
+//     c ^ ((r >> 1) & 3), so the 16-lane fragment reads hit distinct banks;
+//   * the fragment reads are plain ds_read_b128 the compiler does not see as
+//     LDS accesses, with explicit waits that the MFMAs depend on: otherwise
+//     it waits for every load in flight before each read (it cannot tell
+//     that they fill other stages), and a fenced barrier would do the same;
+//   * rows past T or H and columns past the split read zero (the buffer
+//     resource's range; an offset past it);
+//   * with few tiles (a skinny T) K is split over blockIdx.z so that the
+//     CUs are filled; each split writes an FP32 partial tile and the splits
+//     are summed in split order by the batched path's sum-and-round kernel.
+// Sums are FP32 in a fixed k order, the same for both tile shapes, so results
+// depend neither on timing nor on the shape chosen.
 #include <type_traits>
 
 #include "common.hpp"
@@ -33,30 +40,28 @@ namespace {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void_t;
 
-constexpr int BK = 64;
-constexpr int LDR = BK + 8;  // LDS row stride, BF16 elements
+constexpr int BK = 32;      // K columns per step
+constexpr int RB = BK * 2;  // bytes per staged row
 
-typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ int slot(int row, int piece) { return piece ^ ((row >> 1) & 3); }
 
-// 16-byte raw buffer load; an offset at or past the resource's size returns 0
-__device__ __forceinline__ uint4 ld_b128(__amdgpu_buffer_rsrc_t r, uint32_t off)
+__device__ __forceinline__ bf16x8_t as_bf16x8(const u32x4_t &u)
 {
-    const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(r, int(off), 0, 0);
-    return make_uint4(v.x, v.y, v.z, v.w);
+    return __builtin_bit_cast(bf16x8_t, u);
 }
 
-__device__ __forceinline__ bf16x8_t to_bf16x8(const uint4 &u)
+// LDS byte offset of a __shared__ object (its flat address keeps the offset
+// in the low 32 bits)
+__device__ __forceinline__ uint32_t lds_offset(const void *p)
 {
-    bf16x8_t r;
-    __builtin_memcpy(&r, &u, 16);
-    return r;
+    return uint32_t(reinterpret_cast<uintptr_t>(p));
 }
 
 }  // namespace
 
-// BM x BN output tile per workgroup of WM x WN waves; each wave owns a
-// (BM/WM) x (BN/WN) block of 16 x 16 MFMA accumulators.
 template <int BM, int BN, int WM, int WN>
 __global__ __launch_bounds__(WM *WN * 64) void ctx_gemm_kernel(const uint16_t *__restrict__ A,
                                                                const uint16_t *__restrict__ W,
@@ -64,60 +69,84 @@ __global__ __launch_bounds__(WM *WN * 64) void ctx_gemm_kernel(const uint16_t *_
                                                                float *__restrict__ P, int M, int N,
                                                                int K, int Ks)
 {
-    constexpr int NT = WM * WN * 64;
+    constexpr int NW = WM * WN;
     constexpr int FM = BM / WM / 16, FN = BN / WN / 16;
-    constexpr int RPP = NT / 8;  // tile rows one pass of global loads covers
-    constexpr int PA = BM / RPP, PW = BN / RPP;
-    static_assert(BM % RPP == 0 && BN % RPP == 0, "tile rows must be whole passes");
-    extern __shared__ uint4 ctx_lds[];
-    uint16_t *sA0 = reinterpret_cast<uint16_t *>(ctx_lds);
-    uint16_t *sW0 = sA0 + 2 * BM * LDR;
+    static_assert(FM == 4, "the staged waits below assume four A fragments per wave");
+    static_assert(FN == 2 || FN == 4, "two or four W fragments per wave");
+    constexpr int RA = BM / NW, RW = BN / NW;  // rows of A and of W each wave stages
+    static_assert(RA % 16 == 0 && RW % 16 == 0, "a load instruction stages 16 rows");
+    constexpr int IA = RA / 16, IW = RW / 16;
+    constexpr int STAGE = (BM + BN) * RB;
+    // two newer stages may stay in flight when a step's stage must be in
+    constexpr int INFLIGHT = 2 * (IA + IW);
+    __shared__ __attribute__((aligned(1024))) char st0[STAGE];
+    __shared__ __attribute__((aligned(1024))) char st1[STAGE];
+    __shared__ __attribute__((aligned(1024))) char st2[STAGE];
+    __shared__ __attribute__((aligned(1024))) char st3[STAGE];
+    auto stage = [&](auto sc) -> char * {
+        constexpr int S = decltype(sc)::value;
+        if constexpr (S == 0)
+            return st0;
+        else if constexpr (S == 1)
+            return st1;
+        else if constexpr (S == 2)
+            return st2;
+        else
+            return st3;
+    };
+
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wid = tid >> 6;
+    const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wid / WN, wn = wid % WN;
     const int nl = lane & 15, g = lane >> 4;
     const int m0 = blockIdx.y * BM;
     const int n0 = blockIdx.x * BN;
     const int k_begin = blockIdx.z * Ks;
     const int k_end = min(K, k_begin + Ks);
+    const uint32_t rowb = uint32_t(K) * 2;
 
-    // global -> register staging: thread t covers rows t/8 + RPP p, columns
-    // (t%8)*8 .. +8 of the 64-column step.  The tile's rows form a buffer
-    // resource, so rows past M read as zero without a branch, and a column
-    // past the split takes an offset beyond the resource (zero as well).
-    const int lr = tid >> 3;
-    const int lc = (tid & 7) * 8;
-    const uint32_t rowb = uint32_t(K) * 2;  // bytes per row
+    // The tile's rows as buffer resources: rows past M (N) read as zero.
     const __amdgpu_buffer_rsrc_t arsrc = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<uint16_t *>(A) + size_t(m0) * K, 0, int(uint32_t(min(BM, M - m0)) * rowb),
         0x00020000);
     const __amdgpu_buffer_rsrc_t wrsrc = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<uint16_t *>(W) + size_t(n0) * K, 0, int(uint32_t(min(BN, N - n0)) * rowb),
         0x00020000);
-    const uint32_t toff = uint32_t(lr) * rowb + uint32_t(lc) * 2;
-    // two register sets: the loads of step k + 2 are issued before step k is
-    // multiplied, so each load has about two steps of MFMA work to land
-    uint4 ra[2][PA], rw[2][PW];
-    auto gload = [&](int set, int k0) {
-        const uint32_t o = (k0 + lc < k_end) ? toff + uint32_t(k0) * 2 : 0x80000000u;
+    // A load instruction stages 16 rows: lane L takes row L/4 and LDS slot L%4,
+    // which holds piece (L%4) ^ ((row >> 1) & 3) of the row's 64 bytes.
+    const int lrow = lane >> 2;
+    const int lpiece = (lane & 3) ^ ((lrow >> 1) & 3);
+    const uint32_t lofs = uint32_t(lrow) * rowb + uint32_t(lpiece) * 16;
+    auto issue = [&](char *st, int k0) {
+        // a step lies wholly inside or wholly past the split (both multiples of 32)
+        const uint32_t o = k0 < k_end ? lofs + uint32_t(k0) * 2 : 0x80000000u;
 #pragma unroll
-        for (int p = 0; p < PA; ++p)
-            ra[set][p] = ld_b128(arsrc, o + uint32_t(RPP * p) * rowb);
+        for (int j = 0; j < IA; ++j) {
+            const int r0 = wid * RA + 16 * j;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(arsrc, (lds_void_t *)(st + r0 * RB), 16,
+                                                     o + uint32_t(r0) * rowb, 0, 0, 0);
+        }
 #pragma unroll
-        for (int p = 0; p < PW; ++p)
-            rw[set][p] = ld_b128(wrsrc, o + uint32_t(RPP * p) * rowb);
+        for (int j = 0; j < IW; ++j) {
+            const int r0 = wid * RW + 16 * j;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(wrsrc, (lds_void_t *)(st + BM * RB + r0 * RB),
+                                                     16, o + uint32_t(r0) * rowb, 0, 0, 0);
+        }
     };
-    auto sstore = [&](int set, int buf) {
-        uint16_t *sA = sA0 + buf * BM * LDR;
-        uint16_t *sW = sW0 + buf * BN * LDR;
+
+    // fragment addresses inside a stage: lane (g, n) reads row n, piece g
+    uint32_t aoff[FM], woff[FN];
 #pragma unroll
-        for (int p = 0; p < PA; ++p)
-            *reinterpret_cast<uint4 *>(&sA[(lr + RPP * p) * LDR + lc]) = ra[set][p];
+    for (int i = 0; i < FM; ++i) {
+        const int row = (wm * FM + i) * 16 + nl;
+        aoff[i] = uint32_t(row * RB + slot(row, g) * 16);
+    }
 #pragma unroll
-        for (int p = 0; p < PW; ++p)
-            *reinterpret_cast<uint4 *>(&sW[(lr + RPP * p) * LDR + lc]) = rw[set][p];
-    };
+    for (int j = 0; j < FN; ++j) {
+        const int row = (wn * FN + j) * 16 + nl;
+        woff[j] = uint32_t(BM * RB + row * RB + slot(row, g) * 16);
+    }
 
     f32x4_t acc[FM][FN];
 #pragma unroll
@@ -126,55 +155,66 @@ __global__ __launch_bounds__(WM *WN * 64) void ctx_gemm_kernel(const uint16_t *_
         for (int j = 0; j < FN; ++j)
             acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-    auto mma_step = [&](int buf) {
-        const uint16_t *sA = sA0 + buf * BM * LDR;
-        const uint16_t *sW = sW0 + buf * BN * LDR;
+    auto mma_row = [&](auto ic, const u32x4_t &a, const u32x4_t(&w)[FN]) {
+        constexpr int i = decltype(ic)::value;
 #pragma unroll
-        for (int sub = 0; sub < BK / 32; ++sub) {
-            const int kc = sub * 32 + g * 8;
-            bf16x8_t af[FM], wf[FN];
+        for (int j = 0; j < FN; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a), as_bf16x8(w[j]),
+                                                                acc[i][j], 0, 0, 0);
+    };
+    auto compute = [&](const char *st) {
+        const uint32_t base = lds_offset(st);
+        u32x4_t a[FM], w[FN];
 #pragma unroll
-            for (int i = 0; i < FM; ++i)
-                af[i] = to_bf16x8(*reinterpret_cast<const uint4 *>(
-                    &sA[((wm * FM + i) * 16 + nl) * LDR + kc]));
+        for (int j = 0; j < FN; ++j)
+            asm volatile("ds_read_b128 %0, %1" : "=v"(w[j]) : "v"(base + woff[j]));
 #pragma unroll
-            for (int j = 0; j < FN; ++j)
-                wf[j] = to_bf16x8(*reinterpret_cast<const uint4 *>(
-                    &sW[((wn * FN + j) * 16 + nl) * LDR + kc]));
-#pragma unroll
-            for (int i = 0; i < FM; ++i)
-#pragma unroll
-                for (int j = 0; j < FN; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], wf[j], acc[i][j],
-                                                                        0, 0, 0);
-        }
+        for (int i = 0; i < FM; ++i)
+            asm volatile("ds_read_b128 %0, %1" : "=v"(a[i]) : "v"(base + aoff[i]));
+        // W and A row i are in once at most 3 - i reads are outstanding
+        if constexpr (FN == 4)
+            asm volatile("s_waitcnt lgkmcnt(3)"
+                         : "+v"(a[0]), "+v"(w[0]), "+v"(w[1]), "+v"(w[2]), "+v"(w[3]));
+        else
+            asm volatile("s_waitcnt lgkmcnt(3)" : "+v"(a[0]), "+v"(w[0]), "+v"(w[1]));
+        mma_row(std::integral_constant<int, 0>{}, a[0], w);
+        asm volatile("s_waitcnt lgkmcnt(2)" : "+v"(a[1]));
+        mma_row(std::integral_constant<int, 1>{}, a[1], w);
+        asm volatile("s_waitcnt lgkmcnt(1)" : "+v"(a[2]));
+        mma_row(std::integral_constant<int, 2>{}, a[2], w);
+        asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(a[3]));
+        mma_row(std::integral_constant<int, 3>{}, a[3], w);
     };
 
-    // step k lives in register set k & 1 and LDS buffer k & 1
+    using I0 = std::integral_constant<int, 0>;
+    using I1 = std::integral_constant<int, 1>;
+    using I2 = std::integral_constant<int, 2>;
+    using I3 = std::integral_constant<int, 3>;
+    // Step t uses stage t % 4; its loads were issued three steps earlier.  The
+    // barrier after a step (no fence: the newer stages stay in flight) makes
+    // stage t + 1 visible to every wave and frees stage t for step t + 4.
     const int nk = (k_end - k_begin + BK - 1) / BK;
-    gload(0, k_begin);
-    gload(1, k_begin + BK);
-    sstore(0, 0);
-    __syncthreads();
-    // Register sets and LDS buffers alternate, so the loop runs in pairs to
-    // keep every register index a compile-time constant.  Loads and stores
-    // are unconditional (past the split they read zeros and fill a buffer that
-    // is never read), so every path holds the same loads in flight and each
-    // store waits only for its own set.
-    auto step = [&](int kt, auto bc) {
-        constexpr int b = decltype(bc)::value;
-        gload(b, k_begin + (kt + 2) * BK);  // set b was stored to LDS last step
-        __builtin_amdgcn_sched_barrier(0);  // issue the loads before the MFMAs
-        mma_step(b);
-        sstore(b ^ 1, b ^ 1);
-        __syncthreads();
+    issue(stage(I0{}), k_begin);
+    issue(stage(I1{}), k_begin + BK);
+    issue(stage(I2{}), k_begin + 2 * BK);
+    asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(INFLIGHT) : "memory");
+    auto step = [&](int t, auto cur, auto ahead) {
+        issue(stage(ahead), k_begin + (t + 3) * BK);
+        compute(stage(cur));
+        asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(INFLIGHT) : "memory");
     };
-    // an odd count gets one step past the split: zeros, which leave the sums
-    // unchanged (the accumulators start at +0)
-    for (int kt = 0; kt < nk; kt += 2) {
-        step(kt, std::integral_constant<int, 0>{});
-        step(kt + 1, std::integral_constant<int, 1>{});
+    // steps in fours; a count that is not a multiple of four runs up to three
+    // steps past the split, which read zeros and leave the sums unchanged
+    // (the accumulators start at +0)
+#pragma unroll 1
+    for (int t = 0; t < nk; t += 4) {
+        step(t, I0{}, I3{});
+        step(t + 1, I1{}, I0{});
+        step(t + 2, I2{}, I1{});
+        step(t + 3, I3{}, I2{});
     }
+    // every load has landed before the workgroup's LDS is released
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
     // lane (g, n) holds rows 4g..4g+3 of column n of each 16 x 16 tile
 #pragma unroll
@@ -201,40 +241,37 @@ template <int BM, int BN, int WM, int WN>
 hipError_t launch_ctx_tile(const uint16_t *A, const uint16_t *W, uint16_t *C, float *P, int M,
                            int N, int K, CtxSplit sp, hipStream_t s)
 {
-    auto kern = ctx_gemm_kernel<BM, BN, WM, WN>;
-    const size_t lds = size_t(2 * (BM + BN) * LDR) * 2;
-    if (lds > 65536)
-        (void)hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
-                                  hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
     const dim3 grid((N + BN - 1) / BN, (M + BM - 1) / BM, sp.S);
-    hipLaunchKernelGGL(kern, grid, dim3(WM * WN * 64), lds, s, A, W, C, sp.S > 1 ? P : nullptr, M,
-                       N, K, sp.Ks);
+    hipLaunchKernelGGL((ctx_gemm_kernel<BM, BN, WM, WN>), grid, dim3(WM * WN * 64), 0, s, A, W, C,
+                       sp.S > 1 ? P : nullptr, M, N, K, sp.Ks);
     return hipGetLastError();
 }
 
-constexpr int BM = 128, BN = 128;
-
 CtxSplit ctx_split(int M, int N, int K)
 {
-    const long tiles = long((N + BN - 1) / BN) * long((M + BM - 1) / BM);
-    constexpr long kTarget = 512;  // two 256-thread workgroups on each of 256 CUs
-    if (tiles * 4 >= kTarget * 3)
-        return CtxSplit{1, K};
-    int S = int((kTarget + tiles - 1) / tiles);
-    // an even number of 64-column steps per split (the kernel runs them in pairs)
-    int Ks = ((K + S - 1) / S + 2 * BK - 1) / (2 * BK) * (2 * BK);
-    if (Ks < 4 * BK)
-        Ks = 4 * BK;  // at least four K steps per split
+    // The large tile from kCtxBigTileMinRows rows; K split so that about 256
+    // (large: one per CU) or 512 (small: two per CU) workgroups run.
+    const bool big = M >= kCtxBigTileMinRows;
+    const int tm = big ? 256 : 128;
+    const long tiles = long((N + tm - 1) / tm) * long((M + tm - 1) / tm);
+    const long target = big ? 256 : 512;
+    if (tiles * 4 >= target * 3)
+        return CtxSplit{1, K, big};
+    int S = int((target + tiles - 1) / tiles);
+    // a multiple of 128 columns per split, at least four steps
+    int Ks = ((K + S - 1) / S + 127) / 128 * 128;
     if (Ks > K)
         Ks = K;
     S = (K + Ks - 1) / Ks;
-    return CtxSplit{S, Ks};
+    return CtxSplit{S, Ks, big};
 }
 
 hipError_t launch_ctx_gemm(const uint16_t *A, const uint16_t *W, uint16_t *C, float *P, int M,
                            int N, int K, CtxSplit sp, hipStream_t s)
 {
-    return launch_ctx_tile<BM, BN, 4, 2>(A, W, C, P, M, N, K, sp, s);
+    if (sp.big)
+        return launch_ctx_tile<256, 256, 4, 4>(A, W, C, P, M, N, K, sp, s);
+    return launch_ctx_tile<128, 128, 2, 4>(A, W, C, P, M, N, K, sp, s);
 }
 
 }  // namespace mtp

@@ -58,12 +58,16 @@ def check_eh_proj_rows(xg: np.ndarray, x_un: np.ndarray, concat: np.ndarray,
     the K exact BF16 x BF16 products; 2^-12 m covers the few concat entries
     whose FP32 norm rounds to the neighbouring BF16 (each moves the sum by at
     most 2^-7 |W_ik c_k|).  Near-total cancellation (|o| << m) makes a plain
-    ulp bound meaningless there, hence the m-scaled terms.  Then, over all
-    elements: >= 98% bit-equal to the oracle's BF16 x and >= 99.5% within one
-    ulp.  (One concat entry that rounds the other way shifts its whole row by
-    W_ik ulp(c_k), so a few rows can carry several one- and two-ulp moves; a
-    lost or doubled term moves most elements of every row by several ulps.)
-    Returns the statistics."""
+    ulp bound meaningless there, hence the m-scaled terms.
+
+    Then the share of elements not bit-equal to the oracle's BF16 x, per row:
+    under half of any row and 1% of the median row, and at most 0.5% of the
+    median row more than one ulp away.  A concat entry that rounds the other
+    way shifts its whole row by W_ik ulp(c_k), which moves up to about a tenth
+    of that row's elements by an ulp at H = 6144 and a sixth at H = 256 (one
+    term is a larger share of a shorter sum); such rows are a minority.
+    A lost or doubled term, a shifted K step or a wrong tile moves most
+    elements of every row by several ulps.  Returns the statistics."""
     g = bits_to_f64(xg)
     o = np.asarray(x_un, dtype=np.float64)
     K = concat.shape[-1]
@@ -77,10 +81,16 @@ def check_eh_proj_rows(xg: np.ndarray, x_un: np.ndarray, concat: np.ndarray,
     assert np.all(err <= bound), (worst, err[worst], bound[worst], o[worst], m[worst])
     from oracle import bf16_from_f64  # only the rounding of the oracle's own value
     d = np.abs(bf16_order_key(xg) - bf16_order_key(bf16_from_f64(o)))
+    d = d.reshape(-1, d.shape[-1])
+    ne_row = np.mean(d != 0, axis=1)
+    over_row = np.mean(d > 1, axis=1)
     stats = {"elements": int(d.size), "not_equal": float(np.mean(d != 0)),
-             "over_1ulp": float(np.mean(d > 1)), "max_ulps": int(d.max())}
-    assert stats["not_equal"] < 0.02, stats
-    assert stats["over_1ulp"] < 0.005, stats
+             "max_row_not_equal": float(ne_row.max()),
+             "median_row_not_equal": float(np.median(ne_row)),
+             "median_row_over_1ulp": float(np.median(over_row)), "max_ulps": int(d.max())}
+    assert stats["max_row_not_equal"] < 0.5, stats
+    assert stats["median_row_not_equal"] < 0.01, stats
+    assert stats["median_row_over_1ulp"] < 0.005, stats
     return stats
 
 

@@ -17,7 +17,7 @@ from tests import harness
 pytestmark = pytest.mark.gpu
 
 
-def _run(H, V, T, seed, bad_row=None):
+def _run(H, V, T, seed, bad_row=None, sample=None):
     import mtp_draft_head_embed_amd as mtp
     print(f"\n[context] H={H} V={V} T={T} seed={seed}", flush=True)
     cfg = synth.custom(H, V, T + 1, seed)
@@ -34,10 +34,11 @@ def _run(H, V, T, seed, bad_row=None):
     mtp.mtp_context_rows(dw.w, T, tk, hd, x, ws)
     torch.cuda.synchronize()
     xg = harness.bf16_bits(x)
-    ref = oracle.context_rows(wts, tokens, hiddens)
-    rows = [r for r in range(T) if r != bad_row]
-    st = harness.check_eh_proj_rows(xg[rows], ref["x_unrounded"][rows], ref["concat"][rows],
-                                    wts["eh_proj"])
+    rows = [r for r in (range(T) if sample is None else sample) if r != bad_row]
+    # the oracle on the chosen rows only: row r needs tokens[r + 1] and hiddens[r]
+    sub_tok = np.concatenate([[0], tokens[np.array(rows) + 1]]).astype(tokens.dtype)
+    ref = oracle.context_rows(wts, sub_tok, np.ascontiguousarray(hiddens[rows]))
+    st = harness.check_eh_proj_rows(xg[rows], ref["x_unrounded"], ref["concat"], wts["eh_proj"])
     print(f"[context] {st}", flush=True)
     return xg
 
@@ -46,7 +47,7 @@ def _run(H, V, T, seed, bad_row=None):
     (256, 3000, 1, 80), (256, 3000, 2, 81), (256, 3000, 16, 92), (256, 3000, 17, 93),
     (256, 3000, 37, 82), (256, 3000, 64, 83),
     (256, 3000, 65, 84), (256, 3000, 200, 85), (1040, 2000, 65, 86), (1040, 2000, 130, 87),
-    (512, 4000, 300, 88),
+    (512, 4000, 300, 88), (1040, 2000, 600, 94), (256, 3000, 255, 95), (256, 3000, 256, 96),
 ])
 def test_context_rows(H, V, T, seed):
     _run(H, V, T, seed)
@@ -61,3 +62,11 @@ def test_context_rows_out_of_range_token():
 @pytest.mark.slow
 def test_context_rows_large_hidden():
     _run(6144, 20000, 70, 91)
+
+
+@pytest.mark.slow
+def test_context_rows_large_big_tile():
+    """H = 6144, T = 600: the 256 x 256 tile with K split four ways; sampled rows
+    on both sides of every row-tile edge, checked against the oracle."""
+    _run(6144, 20000, 600, 97, sample=[0, 1, 127, 128, 254, 255, 256, 257, 383, 384, 511, 512,
+                                       513, 598, 599])
