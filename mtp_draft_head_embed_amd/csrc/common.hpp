@@ -178,32 +178,57 @@ __device__ __forceinline__ void norm_to_lds(const uint4 (&v)[4], const uint16_t 
     }
 }
 
-// Two vanilla norms in one workgroup with one round trip: the two vectors and
-// their weights are loaded up front and both sums of squares share one block
-// reduction.  dst0[j] = BF16(x0_j w0_j / r0), dst1[j] = BF16(x1_j w1_j / r1);
-// a vector with valid == false is read as zeros.  (dst in LDS or global.)
-__device__ __forceinline__ void dual_norm(const uint16_t *__restrict__ x0, bool valid0,
-                                          const uint16_t *__restrict__ w0,
-                                          const uint16_t *__restrict__ x1,
-                                          const uint16_t *__restrict__ w1, int n, float eps,
-                                          uint16_t *dst0, uint16_t *dst1, float *red)
+// The vanilla norms of the prologues, in two phases: *_load issues every
+// load a thread needs (up to 4 x 8 elements of each vector, n <= 32
+// blockDim.x), *_store reduces across the block and writes the normed BF16
+// vector.  A kernel can issue its own first weight loads between the two:
+// load completion is counted in issue order, so loads issued after the
+// norm's do not hold up its reduction, while the reverse would.
+__device__ __forceinline__ uint4 zero_unless(bool keep, const uint4 &v)
+{
+    return make_uint4(keep ? v.x : 0u, keep ? v.y : 0u, keep ? v.z : 0u, keep ? v.w : 0u);
+}
+
+struct DualNormIn {
+    uint4 a[4], b[4], wa[4], wb[4];
+};
+struct SingleNormIn {
+    uint4 a[4], wa[4];
+};
+
+// [norm(x0) with w0 | norm(x1) with w1], one block reduction for both
+// (x0 reads as zeros when !valid0).
+__device__ __forceinline__ DualNormIn dual_norm_load(const uint16_t *__restrict__ x0, bool valid0,
+                                                     const uint16_t *__restrict__ w0,
+                                                     const uint16_t *__restrict__ x1,
+                                                     const uint16_t *__restrict__ w1, int n)
 {
     const int tid = threadIdx.x;
-    uint4 a[4], b[4], wa[4], wb[4];
+    DualNormIn v;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const int j = (i * blockDim.x + tid) * 8;
+        // load from a clamped index and select, rather than branch around
+        // the load (which would blur the wait counts of the loads after it)
         const bool in = j < n;
-        a[i] = (in && valid0) ? *reinterpret_cast<const uint4 *>(x0 + j) : make_uint4(0, 0, 0, 0);
-        b[i] = in ? *reinterpret_cast<const uint4 *>(x1 + j) : make_uint4(0, 0, 0, 0);
-        wa[i] = in ? *reinterpret_cast<const uint4 *>(w0 + j) : make_uint4(0, 0, 0, 0);
-        wb[i] = in ? *reinterpret_cast<const uint4 *>(w1 + j) : make_uint4(0, 0, 0, 0);
+        const int jc = in ? j : 0;
+        v.a[i] = zero_unless(in && valid0, *reinterpret_cast<const uint4 *>(x0 + jc));
+        v.b[i] = zero_unless(in, *reinterpret_cast<const uint4 *>(x1 + jc));
+        v.wa[i] = zero_unless(in, *reinterpret_cast<const uint4 *>(w0 + jc));
+        v.wb[i] = zero_unless(in, *reinterpret_cast<const uint4 *>(w1 + jc));
     }
+    return v;
+}
+
+__device__ __forceinline__ void dual_norm_store(const DualNormIn &v, int n, float eps,
+                                                uint16_t *dst0, uint16_t *dst1, float *red)
+{
+    const int tid = threadIdx.x;
     float s0 = 0.f, s1 = 0.f;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        const uint32_t pa[4] = {a[i].x, a[i].y, a[i].z, a[i].w};
-        const uint32_t pb[4] = {b[i].x, b[i].y, b[i].z, b[i].w};
+        const uint32_t pa[4] = {v.a[i].x, v.a[i].y, v.a[i].z, v.a[i].w};
+        const uint32_t pb[4] = {v.b[i].x, v.b[i].y, v.b[i].z, v.b[i].w};
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
             s0 = fmaf(bf16_lo(pa[q]), bf16_lo(pa[q]), s0);
@@ -232,10 +257,10 @@ __device__ __forceinline__ void dual_norm(const uint16_t *__restrict__ x0, bool 
     for (int i = 0; i < 4; ++i) {
         const int j = (i * blockDim.x + tid) * 8;
         if (j < n) {
-            const uint32_t pa[4] = {a[i].x, a[i].y, a[i].z, a[i].w};
-            const uint32_t pb[4] = {b[i].x, b[i].y, b[i].z, b[i].w};
-            const uint32_t qa[4] = {wa[i].x, wa[i].y, wa[i].z, wa[i].w};
-            const uint32_t qb[4] = {wb[i].x, wb[i].y, wb[i].z, wb[i].w};
+            const uint32_t pa[4] = {v.a[i].x, v.a[i].y, v.a[i].z, v.a[i].w};
+            const uint32_t pb[4] = {v.b[i].x, v.b[i].y, v.b[i].z, v.b[i].w};
+            const uint32_t qa[4] = {v.wa[i].x, v.wa[i].y, v.wa[i].z, v.wa[i].w};
+            const uint32_t qb[4] = {v.wb[i].x, v.wb[i].y, v.wb[i].z, v.wb[i].w};
             uint32_t oa[4], ob[4];
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
@@ -250,24 +275,40 @@ __device__ __forceinline__ void dual_norm(const uint16_t *__restrict__ x0, bool 
     }
 }
 
+__device__ __forceinline__ void dual_norm(const uint16_t *__restrict__ x0, bool valid0,
+                                          const uint16_t *__restrict__ w0,
+                                          const uint16_t *__restrict__ x1,
+                                          const uint16_t *__restrict__ w1, int n, float eps,
+                                          uint16_t *dst0, uint16_t *dst1, float *red)
+{
+    dual_norm_store(dual_norm_load(x0, valid0, w0, x1, w1, n), n, eps, dst0, dst1, red);
+}
+
 // One vanilla norm with the vector and its weight loaded together.
-__device__ __forceinline__ void single_norm(const uint16_t *__restrict__ x,
-                                            const uint16_t *__restrict__ w, int n, float eps,
-                                            uint16_t *dst, float *red)
+__device__ __forceinline__ SingleNormIn single_norm_load(const uint16_t *__restrict__ x,
+                                                         const uint16_t *__restrict__ w, int n)
 {
     const int tid = threadIdx.x;
-    uint4 a[4], wa[4];
+    SingleNormIn v;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const int j = (i * blockDim.x + tid) * 8;
         const bool in = j < n;
-        a[i] = in ? *reinterpret_cast<const uint4 *>(x + j) : make_uint4(0, 0, 0, 0);
-        wa[i] = in ? *reinterpret_cast<const uint4 *>(w + j) : make_uint4(0, 0, 0, 0);
+        const int jc = in ? j : 0;
+        v.a[i] = zero_unless(in, *reinterpret_cast<const uint4 *>(x + jc));
+        v.wa[i] = zero_unless(in, *reinterpret_cast<const uint4 *>(w + jc));
     }
+    return v;
+}
+
+__device__ __forceinline__ void single_norm_store(const SingleNormIn &v, int n, float eps,
+                                                  uint16_t *dst, float *red)
+{
+    const int tid = threadIdx.x;
     float s0 = 0.f;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        const uint32_t pa[4] = {a[i].x, a[i].y, a[i].z, a[i].w};
+        const uint32_t pa[4] = {v.a[i].x, v.a[i].y, v.a[i].z, v.a[i].w};
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
             s0 = fmaf(bf16_lo(pa[q]), bf16_lo(pa[q]), s0);
@@ -288,8 +329,8 @@ __device__ __forceinline__ void single_norm(const uint16_t *__restrict__ x,
     for (int i = 0; i < 4; ++i) {
         const int j = (i * blockDim.x + tid) * 8;
         if (j < n) {
-            const uint32_t pa[4] = {a[i].x, a[i].y, a[i].z, a[i].w};
-            const uint32_t qa[4] = {wa[i].x, wa[i].y, wa[i].z, wa[i].w};
+            const uint32_t pa[4] = {v.a[i].x, v.a[i].y, v.a[i].z, v.a[i].w};
+            const uint32_t qa[4] = {v.wa[i].x, v.wa[i].y, v.wa[i].z, v.wa[i].w};
             uint32_t oa[4];
 #pragma unroll
             for (int q = 0; q < 4; ++q)
@@ -298,6 +339,13 @@ __device__ __forceinline__ void single_norm(const uint16_t *__restrict__ x,
             *reinterpret_cast<uint4 *>(dst + j) = make_uint4(oa[0], oa[1], oa[2], oa[3]);
         }
     }
+}
+
+__device__ __forceinline__ void single_norm(const uint16_t *__restrict__ x,
+                                            const uint16_t *__restrict__ w, int n, float eps,
+                                            uint16_t *dst, float *red)
+{
+    single_norm_store(single_norm_load(x, w, n), n, eps, dst, red);
 }
 
 }  // namespace mtp

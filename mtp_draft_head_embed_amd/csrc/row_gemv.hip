@@ -88,7 +88,9 @@ __global__ __launch_bounds__(BS) void row_gemv_kernel(RowGemvArgs a)
     const int b = blockIdx.y;
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
-    const int wid = tid / kWave;
+    // the wave index is uniform across the wave; saying so keeps the row
+    // numbers, and the buffer resources built from them, in scalar registers
+    const int wid = __builtin_amdgcn_readfirstlane(tid / kWave);
     const int K = a.K;
 
     constexpr int EPL = FP8 ? 16 : 8;  // elements per 16-byte load
@@ -112,33 +114,57 @@ __global__ __launch_bounds__(BS) void row_gemv_kernel(RowGemvArgs a)
     const int r_outer = r_inner * RPI;
 
     uint4 wv[RPI][U];
+    // The front (eh_proj: three rows per wave) issues every load and zeroes
+    // the ones past r_end or K after (a row past r_end reads row 0, a column
+    // past K column 0): no branches, so the compiler counts the loads exactly
+    // and the prologue waits only for its own.  The head sweeps (tens of
+    // rows per wave) branch around such loads; measured, the branch-free form
+    // costs them about 5% of bandwidth.
     auto load_group = [&](int r0, int c0) {
 #pragma unroll
         for (int k = 0; k < RPI; ++k) {
             const int r = r0 + k * r_inner;
+            const bool rok = r < r_end;
+            if constexpr (PRO == PRO_FRONT) {
+                const char *row = Wb + size_t(rok ? r : 0) * size_t(K) * ESZ;  // row 0 exists
 #pragma unroll
-            for (int u = 0; u < U; ++u) {
-                const int col = (c0 + u) * CW + lane * EPL;
-                wv[k][u] = make_uint4(0, 0, 0, 0);
-                if (r < r_end && col < K)
-                    wv[k][u] = ld_weights<NT>(Wb + (size_t(r) * size_t(K) + size_t(col)) * ESZ);
+                for (int u = 0; u < U; ++u) {
+                    const int col = (c0 + u) * CW + lane * EPL;
+                    const bool ok = rok && col < K;
+                    const uint4 v = ld_weights<NT>(row + size_t(ok ? col : 0) * ESZ);
+                    wv[k][u] =
+                        make_uint4(ok ? v.x : 0u, ok ? v.y : 0u, ok ? v.z : 0u, ok ? v.w : 0u);
+                }
+            } else {
+#pragma unroll
+                for (int u = 0; u < U; ++u) {
+                    const int col = (c0 + u) * CW + lane * EPL;
+                    wv[k][u] = make_uint4(0, 0, 0, 0);
+                    if (rok && col < K)
+                        wv[k][u] = ld_weights<NT>(Wb + (size_t(r) * size_t(K) + size_t(col)) * ESZ);
+                }
             }
         }
     };
-    // the first group's loads do not depend on the activation: issue them now
-    load_group(r_begin, 0);
-
     // ---- prologue: the BF16 activation vector act[0..K) in LDS -------------
-    if (PRO == PRO_FRONT) {
+    // The first weight group does not depend on the activation, so its loads
+    // are issued before the norm completes.  In the front the norm's loads go
+    // first: completion is counted in issue order, so the norm can finish
+    // while the weights are still arriving.
+    if constexpr (PRO == PRO_FRONT) {
         // K = 2H: [enorm(embed[token]) | hnorm(hidden[b])]
         const int H = K / 2;
         const uint32_t tok = a.tokens[b];
         const bool tok_ok = tok < uint32_t(a.vocab);
         const uint16_t *erow = a.embed + (tok_ok ? size_t(tok) * size_t(H) : 0);
-        dual_norm(erow, tok_ok, a.enorm_w, a.hidden + size_t(b) * H, a.hnorm_w, H, a.eps, act,
-                  act + H, red);
+        const DualNormIn nv =
+            dual_norm_load(erow, tok_ok, a.enorm_w, a.hidden + size_t(b) * H, a.hnorm_w, H);
+        load_group(r_begin, 0);
+        __builtin_amdgcn_sched_barrier(0);  // keep the weight loads ahead of the norm
+        dual_norm_store(nv, H, a.eps, act, act + H, red);
     } else {
-        // K = H: shared_head.norm(x[b])
+        // K = H: shared_head.norm(x[b]), the first weight group in flight
+        load_group(r_begin, 0);
         single_norm(a.xin + size_t(b) * K, a.norm_w, K, a.eps, act, red);
     }
     __syncthreads();
