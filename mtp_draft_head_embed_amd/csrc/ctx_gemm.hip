@@ -7,10 +7,12 @@
 // The page stops each row at the block's KV-cache write (out of scope here).
 // With T rows, eh_proj is a dense GEMM C[T][H] = A[T][2H] . W[H][2H]^T with
 // both operands K-contiguous, HBM-bound for a few hundred rows and bound by
-// the matrix cores beyond.  One kernel, two tile shapes:
+// the matrix cores beyond.  One kernel, three tile shapes:
 //   * 256 x 256 output tile per 16-wave workgroup (one per CU) for many rows,
-//     128 x 128 per 8-wave workgroup (two per CU) for few; every wave owns a
-//     64 x 64 or 64 x 32 block of v_mfma_f32_16x16x32_bf16 accumulators;
+//     128 x 128 per 8-wave workgroup for a hundred or so, 64 x 256 per 4-wave
+//     workgroup for a few dozen (more weight rows staged per step); every
+//     wave owns a 64 x 64 or 64 x 32 block of v_mfma_f32_16x16x32_bf16
+//     accumulators;
 //   * K in steps of 32 columns through four LDS stages, each its own LDS
 //     object; the operands go from HBM straight into LDS (buffer loads with
 //     the LDS flag: no registers, no LDS store instructions), issued three
@@ -26,7 +28,7 @@
 //   * with few tiles (a skinny T) K is split over blockIdx.z so that the
 //     CUs are filled; each split writes an FP32 partial tile and the splits
 //     are summed in split order by the batched path's sum-and-round kernel.
-// Sums are FP32 in a fixed k order, the same for both tile shapes, so results
+// Sums are FP32 in a fixed k order, the same for every tile shape, so results
 // depend neither on timing nor on the shape chosen.
 #include <type_traits>
 
@@ -249,29 +251,37 @@ hipError_t launch_ctx_tile(const uint16_t *A, const uint16_t *W, uint16_t *C, fl
 
 CtxSplit ctx_split(int M, int N, int K)
 {
-    // The large tile from kCtxBigTileMinRows rows; K split so that about 256
-    // (large: one per CU) or 512 (small: two per CU) workgroups run.
-    const bool big = M >= kCtxBigTileMinRows;
-    const int tm = big ? 256 : 128;
-    const long tiles = long((N + tm - 1) / tm) * long((M + tm - 1) / tm);
-    const long target = big ? 256 : 512;
+    // K split so that about 256 (large tile: one per CU) or 512 (the others:
+    // two per CU) workgroups run
+    const int tile = M >= kCtxBigTileMinRows   ? kCtxTile256x256
+                     : M >= kCtxMidTileMinRows ? kCtxTile128x128
+                                               : kCtxTile64x256;
+    const int tm = tile == kCtxTile256x256 ? 256 : tile == kCtxTile128x128 ? 128 : 64;
+    const int tn = tile == kCtxTile128x128 ? 128 : 256;
+    const long tiles = long((N + tn - 1) / tn) * long((M + tm - 1) / tm);
+    const long target = tile == kCtxTile256x256 ? 256 : 512;
     if (tiles * 4 >= target * 3)
-        return CtxSplit{1, K, big};
+        return CtxSplit{1, K, tile};
     int S = int((target + tiles - 1) / tiles);
     // a multiple of 128 columns per split, at least four steps
     int Ks = ((K + S - 1) / S + 127) / 128 * 128;
     if (Ks > K)
         Ks = K;
     S = (K + Ks - 1) / Ks;
-    return CtxSplit{S, Ks, big};
+    return CtxSplit{S, Ks, tile};
 }
 
 hipError_t launch_ctx_gemm(const uint16_t *A, const uint16_t *W, uint16_t *C, float *P, int M,
                            int N, int K, CtxSplit sp, hipStream_t s)
 {
-    if (sp.big)
+    switch (sp.tile) {
+    case kCtxTile256x256:
         return launch_ctx_tile<256, 256, 4, 4>(A, W, C, P, M, N, K, sp, s);
-    return launch_ctx_tile<128, 128, 2, 4>(A, W, C, P, M, N, K, sp, s);
+    case kCtxTile128x128:
+        return launch_ctx_tile<128, 128, 2, 4>(A, W, C, P, M, N, K, sp, s);
+    default:
+        return launch_ctx_tile<64, 256, 1, 4>(A, W, C, P, M, N, K, sp, s);
+    }
 }
 
 }  // namespace mtp

@@ -6,13 +6,14 @@
 
 namespace mtp {
 
-// Context rows: C[M][N] = BF16(A[M][K] . W[N][K]^T) on MFMA in 256 x 256
-// tiles (big) or 128 x 128 tiles, with K split S ways (Ks columns each, a
-// multiple of 128) when the tiles alone would leave CUs idle; then the FP32
-// partials P[S][M][N] are summed by launch_sum_norm.
+// Context rows: C[M][N] = BF16(A[M][K] . W[N][K]^T) on MFMA in one of three
+// tile shapes, with K split S ways (Ks columns each, a multiple of 128) when
+// the tiles alone would leave CUs idle; then the FP32 partials P[S][M][N] are
+// summed by launch_sum_norm.
+enum CtxTile { kCtxTile64x256 = 0, kCtxTile128x128 = 1, kCtxTile256x256 = 2 };
 struct CtxSplit {
     int S, Ks;
-    bool big;
+    int tile;  // CtxTile
 };
 CtxSplit ctx_split(int M, int N, int K);
 hipError_t launch_ctx_gemm(const uint16_t *A, const uint16_t *W, uint16_t *C, float *P, int M,
@@ -20,7 +21,10 @@ hipError_t launch_ctx_gemm(const uint16_t *A, const uint16_t *W, uint16_t *C, fl
 // Rows from which the context rows use the tiled GEMM instead of the batched
 // split-K sweep.
 constexpr int kCtxGemmMinRows = 17;
-// Rows from which the GEMM uses the 256 x 256 tile.
+// Rows from which the GEMM uses the 128 x 128 tile (below: 64 x 256, which
+// stages more weight rows per step when few activation rows are needed) and
+// the 256 x 256 tile.
+constexpr int kCtxMidTileMinRows = 65;
 constexpr int kCtxBigTileMinRows = 256;
 
 }  // namespace mtp
