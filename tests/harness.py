@@ -52,16 +52,19 @@ def check_eh_proj_rows(xg: np.ndarray, x_un: np.ndarray, concat: np.ndarray,
     """Compare BF16 eh_proj outputs from the library (bits [T][H]) with the
     oracle's unrounded FP64 values for the same rows.
 
-    Every element: |g - o| <= ulp(max(|g|, |o|)) / 2 + (K 2^-24 + 2^-12) m,
-    m = sum_k |W_ik c_k| over the oracle's concat c and K = 2H.  The first term
-    is the final BF16 rounding; K 2^-24 m bounds FP32 recursive summation of
-    the K exact BF16 x BF16 products; 2^-12 m covers the few concat entries
-    whose FP32 norm rounds to the neighbouring BF16 (each moves the sum by at
-    most 2^-7 |W_ik c_k|).  Near-total cancellation (|o| << m) makes a plain
-    ulp bound meaningless there, hence the m-scaled terms.
+    Every element: |g - o| <= ulp(max(|g|, |o|)) / 2 + K 2^-24 m' + f, with
+    c the oracle's concat, K = 2H, f = sum_k |W_ik| ulp(c_k) and
+    m' = sum_k |W_ik| |c_k| + f.  The first term is the final BF16 rounding;
+    K 2^-24 m' bounds FP32 recursive summation of the K exact BF16 x BF16
+    products of the library's own concat c'; f bounds the effect of c' != c:
+    the library's FP32 norms are accurate to far better than a BF16 ulp, so
+    each c'_k is c_k or a neighbour.  Near-total cancellation (|o| << m')
+    makes a plain ulp bound meaningless there, hence the m-scaled terms; with
+    short rows (small H) one such neighbour can be a large share of the sum,
+    hence f rather than a fixed fraction of m.
 
     Then the share of elements not bit-equal to the oracle's BF16 x, per row:
-    under half of any row and 1% of the median row, and at most 0.5% of the
+    under half of any row (rows of 256 or more), 1% of the median row, and at most 0.5% of the
     median row more than one ulp away.  A concat entry that rounds the other
     way shifts its whole row by W_ik ulp(c_k), which moves up to about a tenth
     of that row's elements by an ulp at H = 6144 and a sixth at H = 256 (one
@@ -71,11 +74,17 @@ def check_eh_proj_rows(xg: np.ndarray, x_un: np.ndarray, concat: np.ndarray,
     g = bits_to_f64(xg)
     o = np.asarray(x_un, dtype=np.float64)
     K = concat.shape[-1]
-    m = np.abs(bits_to_f64(concat)) @ np.abs(bits_to_f64(eh_proj)).T
-    big = np.maximum(np.abs(g), np.abs(o))
-    e = np.floor(np.log2(np.maximum(big, 2.0 ** -133)))
-    ulp = 2.0 ** (np.maximum(e, -126.0) - 7)
-    bound = 0.5 * ulp + (K * 2.0 ** -24 + 2.0 ** -12) * m
+
+    def bf16_ulp(v):
+        ex = np.floor(np.log2(np.maximum(np.abs(v), 2.0 ** -133)))
+        return 2.0 ** (np.maximum(ex, -126.0) - 7)
+
+    cf = bits_to_f64(concat)
+    absw = np.abs(bits_to_f64(eh_proj))
+    flips = bf16_ulp(cf) @ absw.T
+    m = np.abs(cf) @ absw.T + flips
+    ulp = bf16_ulp(np.maximum(np.abs(g), np.abs(o)))
+    bound = 0.5 * ulp + K * 2.0 ** -24 * m + flips
     err = np.abs(g - o)
     worst = np.unravel_index(np.argmax(err / bound), err.shape)
     assert np.all(err <= bound), (worst, err[worst], bound[worst], o[worst], m[worst])
@@ -88,7 +97,8 @@ def check_eh_proj_rows(xg: np.ndarray, x_un: np.ndarray, concat: np.ndarray,
              "max_row_not_equal": float(ne_row.max()),
              "median_row_not_equal": float(np.median(ne_row)),
              "median_row_over_1ulp": float(np.median(over_row)), "max_ulps": int(d.max())}
-    assert stats["max_row_not_equal"] < 0.5, stats
+    if d.shape[1] >= 256:  # in shorter rows one flipped term can move most elements
+        assert stats["max_row_not_equal"] < 0.5, stats
     assert stats["median_row_not_equal"] < 0.01, stats
     assert stats["median_row_over_1ulp"] < 0.005, stats
     return stats

@@ -99,3 +99,12 @@ def test_chain_invalid_first_token():
 @pytest.mark.slow
 def test_chain_large():
     _run(6144, 154880, 1, 4, 3005)
+
+
+def test_chain_max_steps():
+    """K = 64 (the maximum) chained drafts at a tiny shape."""
+    _run(16, 50, 2, 64, 3006)
+
+
+def test_chain_max_batch():
+    _run(64, 700, 64, 2, 3007)

@@ -72,3 +72,14 @@ def test_context_rows_large_big_tile():
     on both sides of every row-tile edge, checked against the oracle."""
     _run(6144, 20000, 600, 97, sample=[0, 1, 127, 128, 254, 255, 256, 257, 383, 384, 511, 512,
                                        513, 598, 599])
+
+
+def test_context_rows_max_rows():
+    """T = 65 536 (the maximum) at H = 16: 256 row tiles of the large tile."""
+    _run(16, 100, 65536, 99)
+
+
+@pytest.mark.slow
+def test_context_rows_max_hidden():
+    """H = 8192 (the maximum, K = 16 384): sampled rows around the tile edges."""
+    _run(8192, 3000, 300, 100, sample=[0, 63, 64, 127, 128, 255, 256, 299])
