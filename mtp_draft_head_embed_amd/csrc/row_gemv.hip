@@ -76,7 +76,7 @@ __device__ __forceinline__ uint4 ld_weights(const char *p)
     return *reinterpret_cast<const uint4 *>(p);
 }
 
-template <bool FP8, int PRO, int EPI, int RPI, int U, bool NT = true, int BS = 256>
+template <bool FP8, int PRO, int EPI, int RPI, int U, bool NT = true, int BS = 256, bool DB = false>
 __global__ __launch_bounds__(BS) void row_gemv_kernel(RowGemvArgs a)
 {
     extern __shared__ uint4 lds_raw[];
@@ -114,38 +114,40 @@ __global__ __launch_bounds__(BS) void row_gemv_kernel(RowGemvArgs a)
     const int r_outer = r_inner * RPI;
 
     uint4 wv[RPI][U];
-    // The front (eh_proj: three rows per wave) issues every load and zeroes
-    // the ones past r_end or K after (a row past r_end reads row 0, a column
-    // past K column 0): no branches, so the compiler counts the loads exactly
-    // and the prologue waits only for its own.  The head sweeps (tens of
+    // The front (eh_proj: a few rows per wave) issues every load (a row past
+    // r_end reads row 0, a column past K column 0, values that are never
+    // used): no branches and nothing computed from the loaded values at load
+    // time, so the compiler counts the loads exactly and waits for a group
+    // only where it is multiplied.  The head sweeps (tens of
     // rows per wave) branch around such loads; measured, the branch-free form
     // costs them about 5% of bandwidth.
-    auto load_group = [&](int r0, int c0) {
+    auto load_into = [&](uint4(&dst)[RPI][U], int r0, int c0) {
 #pragma unroll
         for (int k = 0; k < RPI; ++k) {
             const int r = r0 + k * r_inner;
             const bool rok = r < r_end;
             if constexpr (PRO == PRO_FRONT) {
+                // the values read in place of a row past r_end or a column past
+                // K are never used: columns past K are skipped by the
+                // multiply-add and rows past r_end are not stored
                 const char *row = Wb + size_t(rok ? r : 0) * size_t(K) * ESZ;  // row 0 exists
 #pragma unroll
                 for (int u = 0; u < U; ++u) {
                     const int col = (c0 + u) * CW + lane * EPL;
-                    const bool ok = rok && col < K;
-                    const uint4 v = ld_weights<NT>(row + size_t(ok ? col : 0) * ESZ);
-                    wv[k][u] =
-                        make_uint4(ok ? v.x : 0u, ok ? v.y : 0u, ok ? v.z : 0u, ok ? v.w : 0u);
+                    dst[k][u] = ld_weights<NT>(row + size_t(col < K ? col : 0) * ESZ);
                 }
             } else {
 #pragma unroll
                 for (int u = 0; u < U; ++u) {
                     const int col = (c0 + u) * CW + lane * EPL;
-                    wv[k][u] = make_uint4(0, 0, 0, 0);
+                    dst[k][u] = make_uint4(0, 0, 0, 0);
                     if (rok && col < K)
-                        wv[k][u] = ld_weights<NT>(Wb + (size_t(r) * size_t(K) + size_t(col)) * ESZ);
+                        dst[k][u] = ld_weights<NT>(Wb + (size_t(r) * size_t(K) + size_t(col)) * ESZ);
                 }
             }
         }
     };
+    auto load_group = [&](int r0, int c0) { load_into(wv, r0, c0); };
     // ---- prologue: the BF16 activation vector act[0..K) in LDS -------------
     // The first weight group does not depend on the activation, so its loads
     // are issued before the norm completes.  In the front the norm's loads go
@@ -172,46 +174,45 @@ __global__ __launch_bounds__(BS) void row_gemv_kernel(RowGemvArgs a)
     // ---- row sweep ---------------------------------------------------------
     float best_v = -INFINITY;
     uint32_t best_i = 0xFFFFFFFFu;
-    bool have_group = true;
+    float acc[RPI];
+#pragma unroll
+    for (int k = 0; k < RPI; ++k)
+        acc[k] = 0.f;
 
-    for (int r0 = r_begin; r0 < r_end; r0 += r_outer) {
-        float acc[RPI];
+    // multiply-add one group of weights into acc
+    auto mac_group = [&](const uint4(&w)[RPI][U], int c0) {
 #pragma unroll
-        for (int k = 0; k < RPI; ++k)
-            acc[k] = 0.f;
-        for (int c0 = 0; c0 < nchunks; c0 += U) {
-            if (!have_group)
-                load_group(r0, c0);
-            have_group = false;
+        for (int u = 0; u < U; ++u) {
+            const int col = (c0 + u) * CW + lane * EPL;
+            if (col < K) {
+                if (!FP8) {
+                    const uint4 av = *reinterpret_cast<const uint4 *>(act + col);
 #pragma unroll
-            for (int u = 0; u < U; ++u) {
-                const int col = (c0 + u) * CW + lane * EPL;
-                if (col < K) {
-                    if (!FP8) {
-                        const uint4 av = *reinterpret_cast<const uint4 *>(act + col);
+                    for (int k = 0; k < RPI; ++k)
+                        acc[k] = dot8_bf16(w[k][u], av, acc[k]);
+                } else {
+                    const uint4 a0 = *reinterpret_cast<const uint4 *>(act + col);
+                    const uint4 a1 = *reinterpret_cast<const uint4 *>(act + col + 8);
 #pragma unroll
-                        for (int k = 0; k < RPI; ++k)
-                            acc[k] = dot8_bf16(wv[k][u], av, acc[k]);
-                    } else {
-                        const uint4 a0 = *reinterpret_cast<const uint4 *>(act + col);
-                        const uint4 a1 = *reinterpret_cast<const uint4 *>(act + col + 8);
-#pragma unroll
-                        for (int k = 0; k < RPI; ++k) {
-                            float s = acc[k];
-                            s = dot4_fp8(wv[k][u].x, a0.x, a0.y, s);
-                            s = dot4_fp8(wv[k][u].y, a0.z, a0.w, s);
-                            s = dot4_fp8(wv[k][u].z, a1.x, a1.y, s);
-                            s = dot4_fp8(wv[k][u].w, a1.z, a1.w, s);
-                            acc[k] = s;
-                        }
+                    for (int k = 0; k < RPI; ++k) {
+                        float s = acc[k];
+                        s = dot4_fp8(w[k][u].x, a0.x, a0.y, s);
+                        s = dot4_fp8(w[k][u].y, a0.z, a0.w, s);
+                        s = dot4_fp8(w[k][u].z, a1.x, a1.y, s);
+                        s = dot4_fp8(w[k][u].w, a1.z, a1.w, s);
+                        acc[k] = s;
                     }
                 }
             }
         }
+    };
+    // the finished rows r0 + k r_inner: round, store, argmax bookkeeping
+    auto finish_rows = [&](int r0) {
 #pragma unroll
         for (int k = 0; k < RPI; ++k) {
             const int r = r0 + k * r_inner;
             const float sum = wave_sum(acc[k]);
+            acc[k] = 0.f;
             if (r < r_end) {
                 if (EPI == EPI_STORE) {
                     if (lane == 0)
@@ -228,6 +229,50 @@ __global__ __launch_bounds__(BS) void row_gemv_kernel(RowGemvArgs a)
                     }
                 }
             }
+        }
+    };
+
+    if constexpr (DB) {
+        // Double-buffered: the wave's groups in order (row pass, then column
+        // group), the next one's loads issued before the current one is
+        // multiplied, so a wave always has a group in flight.  Loads past the
+        // wave's last group read row 0 (valid, cached) and are never used.
+        const int gpr = (nchunks + U - 1) / U;  // groups per row pass
+        const int passes = r_begin < r_end ? (r_end - r_begin + r_outer - 1) / r_outer : 0;
+        const int G = passes * gpr;
+        uint4 wb[RPI][U];
+        auto at = [&](int q, int &r0, int &c0) {
+            const int p = q / gpr;
+            r0 = r_begin + p * r_outer;
+            c0 = (q - p * gpr) * U;
+        };
+        auto consume = [&](const uint4(&w)[RPI][U], int q) {
+            int r0, c0;
+            at(q, r0, c0);
+            mac_group(w, c0);
+            if (c0 + U >= nchunks)
+                finish_rows(r0);
+        };
+        for (int q = 0; q < G; q += 2) {
+            int r1, c1, r2, c2;
+            at(q + 1, r1, c1);
+            load_into(wb, r1, c1);
+            consume(wv, q);
+            at(q + 2, r2, c2);
+            load_into(wv, r2, c2);
+            if (q + 1 < G)
+                consume(wb, q + 1);
+        }
+    } else {
+        bool have_group = true;
+        for (int r0 = r_begin; r0 < r_end; r0 += r_outer) {
+            for (int c0 = 0; c0 < nchunks; c0 += U) {
+                if (!have_group)
+                    load_group(r0, c0);
+                have_group = false;
+                mac_group(wv, c0);
+            }
+            finish_rows(r0);
         }
     }
 
@@ -296,15 +341,15 @@ __global__ __launch_bounds__(256) void argmax_final_kernel(const Partial *__rest
 // Host launchers
 // ---------------------------------------------------------------------------
 
-template <bool FP8, int PRO, int EPI, int RPI, int U>
+template <bool FP8, int PRO, int EPI, int RPI, int U, bool DB = false>
 static hipError_t launch_one(const RowGemvArgs &a, int grid, int batch, hipStream_t s,
                              int *grid_out)
 {
     if (grid_out)
         *grid_out = grid;
     const size_t lds = align256(size_t(a.K) * 2);
-    hipLaunchKernelGGL((row_gemv_kernel<FP8, PRO, EPI, RPI, U>), dim3(grid, batch), dim3(256),
-                       lds, s, a);
+    hipLaunchKernelGGL((row_gemv_kernel<FP8, PRO, EPI, RPI, U, true, 256, DB>), dim3(grid, batch),
+                       dim3(256), lds, s, a);
     return hipGetLastError();
 }
 
@@ -368,9 +413,16 @@ static hipError_t launch_fp8_head(const RowGemvArgs &a, int per_cu, int batch, h
 #undef MTP_FP8
 }
 
+// eh_proj: a few rows per wave, so the groups are double-buffered (half a
+// row each at K = 2H = 12288) to keep every wave streaming; short rows take
+// the single-buffered sweep.
 hipError_t launch_eh_proj(const RowGemvArgs &a, int batch, hipStream_t s)
 {
-    return launch_bf16<PRO_FRONT, EPI_STORE>(a, 2, batch, s, device_cu_count(), nullptr);
+    const int nch = (a.K + 511) / 512;
+    if (nch <= 8)
+        return launch_bf16<PRO_FRONT, EPI_STORE>(a, 2, batch, s, device_cu_count(), nullptr);
+    return launch_one<false, PRO_FRONT, EPI_STORE, 1, 12, true>(
+        a, grid_for(a.N, 1, 2, device_cu_count()), batch, s, nullptr);
 }
 
 hipError_t launch_head(const RowGemvArgs &a, bool fp8, int batch, hipStream_t s)
