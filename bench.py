@@ -185,10 +185,12 @@ def main():
     batched = None
     if not args.no_batched and args.config == "large":
         batched = {}
-        for bname, bcfg, paths in (("B16", synth.CONFIGS["batched"], ("fp8",)),
-                                   ("B8", synth.CONFIGS["neartie"], ("bf16", "fp8"))):
+        for bname, bcfg, paths, nb in (("B16", synth.CONFIGS["batched"], ("fp8",), 16),
+                                       ("B8", synth.CONFIGS["neartie"], ("bf16", "fp8"), 8),
+                                       ("B4", synth.CONFIGS["batched"], ("bf16", "fp8"), 4)):
             btok, bhid = synth.make_inputs(bcfg)
-            Bb = bcfg.batch
+            btok, bhid = btok[:nb], np.ascontiguousarray(bhid[:nb])
+            Bb = nb
             btk = torch.from_numpy(btok.astype(np.uint32).view(np.int32)).to(dev)
             bhd = harness.to_dev_bf16(bhid)
             bdr = torch.empty(Bb, dtype=torch.int32, device=dev)
