@@ -190,27 +190,32 @@ __global__ __launch_bounds__(WPB * 64) void mfma_gemm_kernel(MfmaArgs a)
             raw[2 * j + 1] =
                 *reinterpret_cast<const uint4 *>(xs + nl * 128 + (((4 + g) ^ ((nl >> 1) & 7)) * 16));
         }
+        // Every k-step of the group runs: a step past the chunk has zero
+        // weights (their loads read past the resource) and reads staged
+        // column 0 (finite), so it adds exactly zero.  No per-step branch, so
+        // the compiler can issue the activation reads ahead of the MFMAs
+        // instead of waiting for each one in turn.
 #pragma unroll
         for (int u = 0; u < UK; ++u) {
-            if (s0 + u < nsteps) {
-                bf16x8 wf;
-                if (FP8) {
-                    const uint4 &r = raw[u >> 1];
-                    wf = (u & 1) ? fp8x8_to_bf16(r.z, r.w) : fp8x8_to_bf16(r.x, r.y);
-                } else {
-                    wf = as_bf16x8(raw[u]);
-                }
-                const int lc = FP8 ? ((s0 + u) >> 1) * 64 + g * 16 + ((s0 + u) & 1) * 8
-                                   : (s0 + u) * 32 + g * 8;
+            bf16x8 wf;
+            if (FP8) {
+                const uint4 &r = raw[u >> 1];
+                wf = (u & 1) ? fp8x8_to_bf16(r.z, r.w) : fp8x8_to_bf16(r.x, r.y);
+            } else {
+                wf = as_bf16x8(raw[u]);
+            }
+            const int st = s0 + u;
+            const int lc = st >= nsteps ? 0
+                           : FP8        ? (st >> 1) * 64 + g * 16 + (st & 1) * 8
+                                        : st * 32 + g * 8;
 #pragma unroll
-                for (int bt = 0; bt < NBT; ++bt) {
-                    // padded batch rows only feed output rows that are dropped,
-                    // so they may read any staged row
-                    const int arow = min(bt * 16 + nl, B - 1);
-                    const uint4 av = *reinterpret_cast<const uint4 *>(As + size_t(arow) * rs + lc);
-                    acc[bt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(av), wf, acc[bt], 0, 0,
-                                                                      0);
-                }
+            for (int bt = 0; bt < NBT; ++bt) {
+                // padded batch rows only feed output rows that are dropped,
+                // so they may read any staged row
+                const int arow = min(bt * 16 + nl, B - 1);
+                const uint4 av = *reinterpret_cast<const uint4 *>(As + size_t(arow) * rs + lc);
+                acc[bt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(av), wf, acc[bt], 0, 0,
+                                                                  0);
             }
         }
     };
