@@ -73,7 +73,7 @@ __device__ __forceinline__ bf16x8 fp8x8_to_bf16(uint32_t lo, uint32_t hi)
     return r;
 }
 
-template <bool FP8, int EPI, int NBT, int MAXT, int UK, int WPB, bool MULTI>
+template <bool FP8, int EPI, int NBT, int MAXT, int UK, int WPB, bool MULTI, bool RR = false>
 __global__ __launch_bounds__(WPB * 64) void mfma_gemm_kernel(MfmaArgs a)
 {
     extern __shared__ uint4 lds_raw[];
@@ -102,19 +102,23 @@ __global__ __launch_bounds__(WPB * 64) void mfma_gemm_kernel(MfmaArgs a)
     // this wave's 2 KiB exchange scratch, after the staged activations
     char *xs = reinterpret_cast<char *>(lds_raw) + a.xs_off + wid * 2048;
 
-    // Each wave owns a contiguous, equal share of the rows (balanced in bytes);
-    // its tiles are the 16-row blocks that overlap the share, and rows outside
-    // the share are neither loaded nor reported.
+    // Rows go to waves in one of two ways.  By default each wave owns a
+    // contiguous, equal share of the rows (balanced in bytes); its tiles are
+    // the 16-row blocks that overlap the share, and rows outside the share
+    // are neither loaded nor reported.  With RR (the lm_head sweeps) 16-row
+    // tiles are dealt round-robin to the grid's waves instead, so the grid
+    // streams one window of the matrix at a time: measured 3-7% faster than
+    // 2048 waves each streaming its own region.
     const int Wt = gridDim.x * WPB;
     const int gw = blockIdx.x * WPB + wid;
     const int R = (N + Wt - 1) / Wt;
-    const int r_lo = min(N, gw * R);
-    const int r_hi = min(N, r_lo + R);
+    int r_lo = min(N, gw * R);
+    int r_hi = min(N, r_lo + R);
     const int t_lo = r_lo / 16;
     const int ntiles = r_hi > r_lo ? (r_hi + 15) / 16 - t_lo : 0;
     // The wave's rows as a buffer resource: loads outside [r_lo, r_hi) return
     // zero in hardware, so partial tiles need no per-lane predicates.
-    const __amdgpu_buffer_rsrc_t wrsrc = __builtin_amdgcn_make_buffer_rsrc(
+    __amdgpu_buffer_rsrc_t wrsrc = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<char *>(Wb) + size_t(r_lo) * wrow, 0, int(size_t(r_hi - r_lo) * wrow), 0x00020000);
     // With several K-chunks (MULTI): passes of MAXT tiles whose accumulators
     // live across the chunks; the same pass count in every wave of the
@@ -256,9 +260,21 @@ __global__ __launch_bounds__(WPB * 64) void mfma_gemm_kernel(MfmaArgs a)
         // eh_proj a workgroup per CU.)
         const int kc_len = k_end - k_begin;
         const int nsteps = FP8 ? 2 * ((kc_len + 63) / 64) : (kc_len + 31) / 32;
+        // RR: 16-row tiles dealt round-robin to the grid's waves, so the grid
+        // sweeps one window of the matrix at a time; each tile its own
+        // resource (rows past N read zero)
+        const int t_first = RR ? gw : t_lo;
+        const int t_stop = RR ? (N + 15) / 16 : t_lo + ntiles;
+        const int t_step = RR ? Wt : 1;
 #pragma unroll 1
-        for (int t = 0; t < ntiles; ++t) {
-            const int tile0 = (t_lo + t) * 16;
+        for (int t = t_first; t < t_stop; t += t_step) {
+            const int tile0 = t * 16;
+            if constexpr (RR) {
+                r_lo = tile0;
+                r_hi = min(N, tile0 + 16);
+                wrsrc = __builtin_amdgcn_make_buffer_rsrc(const_cast<char *>(Wb) + size_t(tile0) * wrow,
+                                                          0, int(size_t(r_hi - r_lo) * wrow), 0x00020000);
+            }
             f32x4 acc[NBT];
 #pragma unroll
             for (int bt = 0; bt < NBT; ++bt)
@@ -272,8 +288,23 @@ __global__ __launch_bounds__(WPB * 64) void mfma_gemm_kernel(MfmaArgs a)
             epilogue(acc, tile0);
         }
     } else {
+        // RR as above; the pass count stays the same in every wave of the
+        // workgroup (the chunk barriers), each tile's resource is made again
+        // before its loads and its epilogue
+        const int T16 = (N + 15) / 16;
+        const int nt_w = RR ? (gw < T16 ? (T16 - gw + Wt - 1) / Wt : 0) : ntiles;
+        const int npass_w = RR ? ((T16 + Wt - 1) / Wt + MAXT - 1) / MAXT : npass;
+        auto tile_of = [&](int tix) { return RR ? (gw + tix * Wt) * 16 : (t_lo + tix) * 16; };
+        auto set_tile = [&](int tile0) {
+            if constexpr (RR) {
+                r_lo = tile0;
+                r_hi = min(N, tile0 + 16);
+                wrsrc = __builtin_amdgcn_make_buffer_rsrc(const_cast<char *>(Wb) + size_t(tile0) * wrow,
+                                                          0, int(size_t(r_hi - r_lo) * wrow), 0x00020000);
+            }
+        };
 #pragma unroll 1
-        for (int pass = 0; pass < npass; ++pass) {
+        for (int pass = 0; pass < npass_w; ++pass) {
             f32x4 acc[MAXT][NBT];
 #pragma unroll
             for (int j = 0; j < MAXT; ++j)
@@ -293,9 +324,10 @@ __global__ __launch_bounds__(WPB * 64) void mfma_gemm_kernel(MfmaArgs a)
 #pragma unroll
                 for (int j = 0; j < MAXT; ++j) {
                     const int tix = pass * MAXT + j;
-                    if (tix >= ntiles)
+                    if (tix >= nt_w)
                         continue;  // uniform across the wave
-                    const int tile0 = (t_lo + tix) * 16;
+                    const int tile0 = tile_of(tix);
+                    set_tile(tile0);
                     uint4 raw[NL];
 #pragma unroll 1
                     for (int s0 = 0; s0 < nsteps; s0 += UK) {
@@ -307,8 +339,10 @@ __global__ __launch_bounds__(WPB * 64) void mfma_gemm_kernel(MfmaArgs a)
 #pragma unroll
             for (int j = 0; j < MAXT; ++j) {
                 const int tix = pass * MAXT + j;
-                if (tix < ntiles)
-                    epilogue(acc[j], (t_lo + tix) * 16);
+                if (tix < nt_w) {
+                    set_tile(tile_of(tix));
+                    epilogue(acc[j], tile_of(tix));
+                }
             }
         }
     }
@@ -389,8 +423,8 @@ static hipError_t launch_mfma_nbt(MfmaArgs a, int grid, int splits, hipStream_t 
     constexpr int UK = FP8 ? 32 : 16;
     a.KC = chunk_cols(a.B, a.Ks, WPB);
     const bool multi = a.KC < a.Ks;
-    auto kern = multi ? mfma_gemm_kernel<FP8, EPI, NBT, MAXT, UK, WPB, true>
-                      : mfma_gemm_kernel<FP8, EPI, NBT, 1, UK, WPB, false>;
+    auto kern = multi ? mfma_gemm_kernel<FP8, EPI, NBT, MAXT, UK, WPB, true, EPI == EPI_ARGMAX>
+                      : mfma_gemm_kernel<FP8, EPI, NBT, 1, UK, WPB, false, EPI == EPI_ARGMAX>;
     a.xs_off = int(align256(size_t(a.B) * size_t(a.KC + 8) * 2));
     size_t lds = size_t(a.xs_off) + size_t(WPB) * 2048;
     const size_t red = size_t(WPB * 16 * NBT) * 8;
