@@ -419,7 +419,7 @@ static int chunk_cols(int B, int klen, int wpb)
 template <bool FP8, int EPI, int NBT, int WPB>
 static hipError_t launch_mfma_nbt(MfmaArgs a, int grid, int splits, hipStream_t s)
 {
-    constexpr int MAXT = NBT == 1 ? 4 : (NBT == 2 ? 2 : 1);
+    constexpr int MAXT = NBT == 1 ? 6 : (NBT == 2 ? 2 : 1);
     constexpr int UK = FP8 ? 32 : 16;
     a.KC = chunk_cols(a.B, a.Ks, WPB);
     const bool multi = a.KC < a.Ks;
