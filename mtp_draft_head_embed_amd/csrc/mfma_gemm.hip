@@ -125,21 +125,34 @@ __global__ __launch_bounds__(WPB * 64) void mfma_gemm_kernel(MfmaArgs a)
     // workgroup, so the barriers match.
     const int npass = ((R + 15) / 16 + 1 + MAXT - 1) / MAXT;
 
+    // Stage the activations of one K-chunk: up to SB 16-byte loads per thread
+    // are issued before any of them is stored, so the chunk costs about one
+    // memory latency rather than one per load.
     auto stage = [&](int kc0) {
+        constexpr int SB = 8;
         const int kc_len = min(KC, k_end - kc0);
-        for (int i = tid; i < B * (KC / 8); i += NT) {
-            const int bb = i / (KC / 8);
-            const int c = (i - bb * (KC / 8)) * 8;
-            uint4 v = make_uint4(0, 0, 0, 0);
-            if (c < kc_len)
-                v = *reinterpret_cast<const uint4 *>(a.A + size_t(bb) * K + kc0 + c);
-            *reinterpret_cast<uint4 *>(As + size_t(bb) * rs + c) = v;
+        const int n16 = B * (KC / 8);
+        for (int i0 = tid; i0 < n16; i0 += SB * NT) {
+            uint4 v[SB];
+#pragma unroll
+            for (int j = 0; j < SB; ++j) {
+                const int i = i0 + j * NT;
+                const int bb = i / (KC / 8);
+                const int c = (i - bb * (KC / 8)) * 8;
+                v[j] = make_uint4(0, 0, 0, 0);
+                if (i < n16 && c < kc_len)
+                    v[j] = *reinterpret_cast<const uint4 *>(a.A + size_t(bb) * K + kc0 + c);
+            }
+#pragma unroll
+            for (int j = 0; j < SB; ++j) {
+                const int i = i0 + j * NT;
+                const int bb = i / (KC / 8);
+                const int c = (i - bb * (KC / 8)) * 8;
+                if (i < n16)
+                    *reinterpret_cast<uint4 *>(As + size_t(bb) * rs + c) = v[j];
+            }
         }
     };
-    if (!MULTI) {
-        stage(k_begin);
-        __syncthreads();
-    }
 
     float best_v[NBT][4];
     uint32_t best_i[NBT][4];
@@ -266,23 +279,42 @@ __global__ __launch_bounds__(WPB * 64) void mfma_gemm_kernel(MfmaArgs a)
         const int t_first = RR ? gw : t_lo;
         const int t_stop = RR ? (N + 15) / 16 : t_lo + ntiles;
         const int t_step = RR ? Wt : 1;
+        auto set_tile = [&](int tile0) {
+            if constexpr (RR) {
+                // a tile at or past N (a wave with no tile) gets an empty range
+                r_lo = min(N, tile0);
+                r_hi = min(N, tile0 + 16);
+                wrsrc = __builtin_amdgcn_make_buffer_rsrc(const_cast<char *>(Wb) + size_t(r_lo) * wrow,
+                                                          0, int(size_t(r_hi - r_lo) * wrow), 0x00020000);
+            }
+        };
+        // eh_proj (three groups per wave): the first group's weight loads go
+        // out before the activations are staged, so the two latencies overlap
+        // (measured 4 us off the B = 16 sweep).  The long head sweeps measured
+        // 1% slower with it and skip it.  A wave with no tile loads through an
+        // empty or zero-length range: zeros, no memory access.
+        constexpr bool PRE = EPI == EPI_STORE;
+        uint4 raw[NL];
+        if constexpr (PRE) {
+            set_tile(t_first * 16);
+            load_group(raw, t_first * 16, 0, k_begin, kc_len);
+        }
+        stage(k_begin);
+        __syncthreads();
+        bool have = PRE;
 #pragma unroll 1
         for (int t = t_first; t < t_stop; t += t_step) {
             const int tile0 = t * 16;
-            if constexpr (RR) {
-                r_lo = tile0;
-                r_hi = min(N, tile0 + 16);
-                wrsrc = __builtin_amdgcn_make_buffer_rsrc(const_cast<char *>(Wb) + size_t(tile0) * wrow,
-                                                          0, int(size_t(r_hi - r_lo) * wrow), 0x00020000);
-            }
+            set_tile(tile0);
             f32x4 acc[NBT];
 #pragma unroll
             for (int bt = 0; bt < NBT; ++bt)
                 acc[bt] = f32x4{0.f, 0.f, 0.f, 0.f};
-            uint4 raw[NL];
 #pragma unroll 1
             for (int s0 = 0; s0 < nsteps; s0 += UK) {
-                load_group(raw, tile0, s0, k_begin, kc_len);
+                if (!PRE || !have)
+                    load_group(raw, tile0, s0, k_begin, kc_len);
+                have = false;
                 compute_group(raw, acc, s0, nsteps);
             }
             epilogue(acc, tile0);
@@ -297,9 +329,10 @@ __global__ __launch_bounds__(WPB * 64) void mfma_gemm_kernel(MfmaArgs a)
         auto tile_of = [&](int tix) { return RR ? (gw + tix * Wt) * 16 : (t_lo + tix) * 16; };
         auto set_tile = [&](int tile0) {
             if constexpr (RR) {
-                r_lo = tile0;
+                // a tile at or past N (a wave with no tile) gets an empty range
+                r_lo = min(N, tile0);
                 r_hi = min(N, tile0 + 16);
-                wrsrc = __builtin_amdgcn_make_buffer_rsrc(const_cast<char *>(Wb) + size_t(tile0) * wrow,
+                wrsrc = __builtin_amdgcn_make_buffer_rsrc(const_cast<char *>(Wb) + size_t(r_lo) * wrow,
                                                           0, int(size_t(r_hi - r_lo) * wrow), 0x00020000);
             }
         };
@@ -313,14 +346,22 @@ __global__ __launch_bounds__(WPB * 64) void mfma_gemm_kernel(MfmaArgs a)
                     acc[j][bt] = f32x4{0.f, 0.f, 0.f, 0.f};
             for (int ch = 0; ch < nchunks; ++ch) {
                 const int kc0 = k_begin + ch * KC;
-                __syncthreads();  // the previous chunk's LDS reads are done
-                stage(kc0);
-                __syncthreads();
                 const int kc_len = min(KC, k_end - kc0);  // a multiple of 16
                 // k-steps of 32 columns.  FP8 loads cover a pair of steps (64
                 // columns), so the FP8 count is a whole number of pairs; columns
                 // past the chunk are zero in LDS and not loaded from HBM.
                 const int nsteps = FP8 ? 2 * ((kc_len + 63) / 64) : (kc_len + 31) / 32;
+                __syncthreads();  // the previous chunk's LDS reads are done
+                // the pass's first group goes out with the staging loads
+                uint4 raw[NL];
+                const bool pre = pass * MAXT < nt_w;
+                if (pre) {
+                    set_tile(tile_of(pass * MAXT));
+                    load_group(raw, tile_of(pass * MAXT), 0, kc0, kc_len);
+                }
+                stage(kc0);
+                __syncthreads();
+                bool have = pre;
 #pragma unroll
                 for (int j = 0; j < MAXT; ++j) {
                     const int tix = pass * MAXT + j;
@@ -328,10 +369,11 @@ __global__ __launch_bounds__(WPB * 64) void mfma_gemm_kernel(MfmaArgs a)
                         continue;  // uniform across the wave
                     const int tile0 = tile_of(tix);
                     set_tile(tile0);
-                    uint4 raw[NL];
 #pragma unroll 1
                     for (int s0 = 0; s0 < nsteps; s0 += UK) {
-                        load_group(raw, tile0, s0, kc0, kc_len);
+                        if (!have)
+                            load_group(raw, tile0, s0, kc0, kc_len);
+                        have = false;
                         compute_group(raw, acc[j], s0, nsteps);
                     }
                 }
@@ -419,7 +461,12 @@ static int chunk_cols(int B, int klen, int wpb)
 template <bool FP8, int EPI, int NBT, int WPB>
 static hipError_t launch_mfma_nbt(MfmaArgs a, int grid, int splits, hipStream_t s)
 {
-    constexpr int MAXT = NBT == 1 ? 6 : (NBT == 2 ? 2 : 1);
+    // Tiles per pass with several K-chunks: every pass restages the chunks,
+    // so one pass should cover a wave's tiles.  The Large lm_head deals ~5
+    // tiles to each of 2048 waves; 6 keeps B <= 16 to one pass (measured 2%
+    // faster than 4 at B = 16 FP8) without spilling.  The split-K eh_proj
+    // runs 3 workgroups per CU and keeps 4 (fewer registers).
+    constexpr int MAXT = NBT == 1 ? (EPI == EPI_ARGMAX ? 6 : 4) : (NBT == 2 ? 2 : 1);
     constexpr int UK = FP8 ? 32 : 16;
     a.KC = chunk_cols(a.B, a.Ks, WPB);
     const bool multi = a.KC < a.Ks;
