@@ -262,7 +262,11 @@ CtxSplit ctx_split(int M, int N, int K)
     const long target = tile == kCtxTile256x256 ? 256 : 512;
     if (tiles * 4 >= target * 3)
         return CtxSplit{1, K, tile};
-    int S = int((target + tiles - 1) / tiles);
+    // the most splits whose workgroups all run at once: one more leaves a
+    // second, nearly empty round of workgroups
+    int S = int(target / tiles);
+    if (S < 1)
+        S = 1;
     // a multiple of 128 columns per split, at least four steps
     int Ks = ((K + S - 1) / S + 127) / 128 * 128;
     if (Ks > K)
