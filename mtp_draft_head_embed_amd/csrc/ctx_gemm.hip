@@ -251,8 +251,8 @@ hipError_t launch_ctx_tile(const uint16_t *A, const uint16_t *W, uint16_t *C, fl
 
 CtxSplit ctx_split(int M, int N, int K)
 {
-    // K split so that about 256 (large tile: one per CU) or 512 (the others:
-    // two per CU) workgroups run
+    // K split so that at most 256 (large tile: one per CU) or 512 (the
+    // others: two per CU) workgroups run, all in one round
     const int tile = M >= kCtxBigTileMinRows   ? kCtxTile256x256
                      : M >= kCtxMidTileMinRows ? kCtxTile128x128
                                                : kCtxTile64x256;
