@@ -7,11 +7,12 @@
 // The page stops each row at the block's KV-cache write (out of scope here).
 // With T rows, eh_proj is a dense GEMM C[T][H] = A[T][2H] . W[H][2H]^T with
 // both operands K-contiguous, HBM-bound for a few hundred rows and bound by
-// the matrix cores beyond.  One kernel, three tile shapes:
-//   * 256 x 256 output tile per 16-wave workgroup (one per CU) for many rows,
-//     128 x 128 per 8-wave workgroup for a hundred or so, 64 x 256 per 4-wave
-//     workgroup for a few dozen (more weight rows staged per step); every
-//     wave owns a 64 x 64 or 64 x 32 block of v_mfma_f32_16x16x32_bf16
+// the matrix cores beyond.  One kernel, four tile shapes:
+//   * 256 x 256 or 256 x 192 output tile per 16-wave workgroup (one per CU)
+//     for many rows (whichever fills the CUs in whole rounds), 128 x 128 per
+//     8-wave workgroup for a hundred or so, 64 x 256 per 4-wave workgroup
+//     for a few dozen (more weight rows staged per step); every wave owns a
+//     64 x 64, 64 x 48 or 64 x 32 block of v_mfma_f32_16x16x32_bf16
 //     accumulators;
 //   * K in steps of 32 columns through four LDS stages, each its own LDS
 //     object; the operands go from HBM straight into LDS (buffer loads with
@@ -74,11 +75,20 @@ __global__ __launch_bounds__(WM *WN * 64) void ctx_gemm_kernel(const uint16_t *_
     constexpr int NW = WM * WN;
     constexpr int FM = BM / WM / 16, FN = BN / WN / 16;
     static_assert(FM == 4, "the staged waits below assume four A fragments per wave");
-    static_assert(FN == 2 || FN == 4, "two or four W fragments per wave");
-    constexpr int RA = BM / NW, RW = BN / NW;  // rows of A and of W each wave stages
-    static_assert(RA % 16 == 0 && RW % 16 == 0, "a load instruction stages 16 rows");
+    static_assert(FN >= 2 && FN <= 4, "two to four W fragments per wave");
+    // A load instruction stages 16 rows.  The A rows go to the waves in equal
+    // contiguous shares; so do the W rows when they divide evenly, else W row
+    // group q (16 rows) goes to wave q, and the waves past the last group
+    // stage nothing real: their load reads past the resource (zeros) into a
+    // 1 KiB slot past the stage, so every wave issues the same number of
+    // loads per step and the vmcnt waits below hold for all of them.
+    constexpr int RA = BM / NW;
+    static_assert(RA % 16 == 0 && BN % 16 == 0, "a load instruction stages 16 rows");
+    constexpr bool WSPLIT = (BN / NW) % 16 == 0;
+    static_assert(WSPLIT || BN / 16 <= NW, "uneven W staging takes one group per wave");
+    constexpr int RW = WSPLIT ? BN / NW : 16;
     constexpr int IA = RA / 16, IW = RW / 16;
-    constexpr int STAGE = (BM + BN) * RB;
+    constexpr int STAGE = (BM + BN) * RB + (WSPLIT ? 0 : (NW - BN / 16) * 16 * RB);
     // two newer stages may stay in flight when a step's stage must be in
     constexpr int INFLIGHT = 2 * (IA + IW);
     __shared__ __attribute__((aligned(1024))) char st0[STAGE];
@@ -132,8 +142,11 @@ __global__ __launch_bounds__(WM *WN * 64) void ctx_gemm_kernel(const uint16_t *_
 #pragma unroll
         for (int j = 0; j < IW; ++j) {
             const int r0 = wid * RW + 16 * j;
+            // uneven W staging: a wave past the last group fills its own slot
+            // after the stage's W rows with zeros (an offset past the range)
+            const uint32_t ow = (WSPLIT || r0 < BN) ? o + uint32_t(r0) * rowb : 0x80000000u;
             __builtin_amdgcn_raw_ptr_buffer_load_lds(wrsrc, (lds_void_t *)(st + BM * RB + r0 * RB),
-                                                     16, o + uint32_t(r0) * rowb, 0, 0, 0);
+                                                     16, ow, 0, 0, 0);
         }
     };
 
@@ -177,6 +190,8 @@ __global__ __launch_bounds__(WM *WN * 64) void ctx_gemm_kernel(const uint16_t *_
         if constexpr (FN == 4)
             asm volatile("s_waitcnt lgkmcnt(3)"
                          : "+v"(a[0]), "+v"(w[0]), "+v"(w[1]), "+v"(w[2]), "+v"(w[3]));
+        else if constexpr (FN == 3)
+            asm volatile("s_waitcnt lgkmcnt(3)" : "+v"(a[0]), "+v"(w[0]), "+v"(w[1]), "+v"(w[2]));
         else
             asm volatile("s_waitcnt lgkmcnt(3)" : "+v"(a[0]), "+v"(w[0]), "+v"(w[1]));
         mma_row(std::integral_constant<int, 0>{}, a[0], w);
@@ -249,17 +264,11 @@ hipError_t launch_ctx_tile(const uint16_t *A, const uint16_t *W, uint16_t *C, fl
     return hipGetLastError();
 }
 
-CtxSplit ctx_split(int M, int N, int K)
+// K split of one tile shape: at most `target` workgroups (256 for the large
+// tiles, one per CU; 512 for the others, two per CU), all in one round.
+static CtxSplit split_for(int M, int N, int K, int tile, int tm, int tn, long target)
 {
-    // K split so that at most 256 (large tile: one per CU) or 512 (the
-    // others: two per CU) workgroups run, all in one round
-    const int tile = M >= kCtxBigTileMinRows   ? kCtxTile256x256
-                     : M >= kCtxMidTileMinRows ? kCtxTile128x128
-                                               : kCtxTile64x256;
-    const int tm = tile == kCtxTile256x256 ? 256 : tile == kCtxTile128x128 ? 128 : 64;
-    const int tn = tile == kCtxTile128x128 ? 128 : 256;
     const long tiles = long((N + tn - 1) / tn) * long((M + tm - 1) / tm);
-    const long target = tile == kCtxTile256x256 ? 256 : 512;
     if (tiles * 4 >= target * 3)
         return CtxSplit{1, K, tile};
     // the most splits whose workgroups all run at once: one more leaves a
@@ -275,12 +284,33 @@ CtxSplit ctx_split(int M, int N, int K)
     return CtxSplit{S, Ks, tile};
 }
 
+CtxSplit ctx_split(int M, int N, int K)
+{
+    if (M < kCtxMidTileMinRows)
+        return split_for(M, N, K, kCtxTile64x256, 64, 256, 512);
+    if (M < kCtxBigTileMinRows)
+        return split_for(M, N, K, kCtxTile128x128, 128, 128, 512);
+    // 256 x 256 or 256 x 192, whichever finishes in less tile work: rounds
+    // of 256 workgroups times the work of one workgroup (at H = 6144 the
+    // 192-wide tile turns 192 or 384 workgroups into whole rounds of 256 or
+    // 512)
+    const CtxSplit a = split_for(M, N, K, kCtxTile256x256, 256, 256, 256);
+    const CtxSplit b = split_for(M, N, K, kCtxTile256x192, 256, 192, 256);
+    auto work = [&](const CtxSplit &c, int tn) {
+        const long wgs = long((N + tn - 1) / tn) * long((M + 255) / 256) * c.S;
+        return ((wgs + 255) / 256) * long(c.Ks) * tn;
+    };
+    return work(b, 192) < work(a, 256) ? b : a;
+}
+
 hipError_t launch_ctx_gemm(const uint16_t *A, const uint16_t *W, uint16_t *C, float *P, int M,
                            int N, int K, CtxSplit sp, hipStream_t s)
 {
     switch (sp.tile) {
     case kCtxTile256x256:
         return launch_ctx_tile<256, 256, 4, 4>(A, W, C, P, M, N, K, sp, s);
+    case kCtxTile256x192:
+        return launch_ctx_tile<256, 192, 4, 4>(A, W, C, P, M, N, K, sp, s);
     case kCtxTile128x128:
         return launch_ctx_tile<128, 128, 2, 4>(A, W, C, P, M, N, K, sp, s);
     default:
