@@ -99,6 +99,58 @@ def test_quantiser_exhaustive_rows():
     assert bads.size == 0, [(hex(rows[i, 0]), sg[i], ref[1][i]) for i in bads[:5]]
 
 
+def _midpoint_rows(amax_lo, amax_hi, width=2.0 ** -12):
+    """Rows [a, w1..w15] (|w| <= a, so the scale is fl32(a / 448)) whose
+    quotients w / s lie within `width` of an E4M3 rounding midpoint, measured
+    in units of the code spacing: exact ties where s has few significant bits,
+    near ties (a few float32 units off) elsewhere, and some just outside the
+    window the kernel hands to the division."""
+    b = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    f = (b.astype(np.uint32) << 16).view(np.float32)
+    fin = np.isfinite(f) & (f != 0)
+    avals = b[fin & (f >= amax_lo) & (f < amax_hi)]
+    rows = []
+    for a16 in avals:
+        a = np.float64(np.float32((np.uint32(a16) << 16).view(np.float32)))
+        s = np.float64(np.float32(a) / np.float32(448.0))
+        ws = b[fin & (np.abs(f) <= a)]
+        qv = np.abs(f[fin & (np.abs(f) <= a)].astype(np.float64) / s)
+        nrm = qv >= 2.0 ** -6
+        e = np.floor(np.log2(np.where(nrm, qv, 1.0)))
+        k = np.where(nrm, (qv / 2.0 ** e - 1.0) * 16.0, qv * 1024.0)  # midpoints at odd k
+        d = np.abs(k - (2.0 * np.floor(k / 2.0) + 1.0))
+        pick = ws[(d < width) & (qv > 0)]
+        for i in range(0, pick.size, 15):
+            r = np.zeros(16, np.uint16)
+            r[0] = a16
+            r[1:1 + pick[i:i + 15].size] = pick[i:i + 15]
+            rows.append(r)
+    return np.array(rows, np.uint16)
+
+
+def test_quantiser_midpoint_quotients():
+    """Scales that are not powers of two (so 1/s is inexact) with quotients at
+    or next to E4M3 rounding midpoints, including rows on both sides of the
+    scale range where the kernel divides every element: codes and scales
+    bit-exact against the oracle."""
+    _say("\n[quantiser] near-midpoint quotients")
+    rows = np.concatenate([_midpoint_rows(448.0, 896.0), _midpoint_rows(1.0, 2.0),
+                           _midpoint_rows(2.0 ** -112, 2.0 ** -110)])
+    assert rows.shape[0] > 500
+    ref = oracle.quantize_fp8(rows)
+    V, H = rows.shape
+    import mtp_draft_head_embed_amd as mtp
+    q = torch.empty((V, H), dtype=torch.uint8, device="cuda")
+    s = torch.empty(V, dtype=torch.float32, device="cuda")
+    ws = torch.empty(256, dtype=torch.uint8, device="cuda")
+    mtp.mtp_quantize_head_fp8(harness.to_dev_bf16(rows), V, H, q, s, ws)
+    qg, sg = q.cpu().numpy(), s.cpu().numpy()
+    bad = np.argwhere(qg != ref[0])
+    assert bad.size == 0, [(hex(rows[i, 0]), hex(rows[i, j]), hex(qg[i, j]), hex(ref[0][i, j]))
+                           for i, j in bad[:5]]
+    assert np.array_equal(sg.view(np.uint32), ref[1].view(np.uint32))
+
+
 def test_quantiser_nonfinite():
     import mtp_draft_head_embed_amd as mtp
     for bad in (0x7F80, 0xFF80, 0x7FC0):
