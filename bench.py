@@ -126,6 +126,27 @@ def main():
     q, s = harness.quantize_dev(dw)
     torch.cuda.synchronize()
 
+    # the load-time FP8 copy of lm_head (timed apart from the sweep): reads the
+    # BF16 matrix, writes the codes and the per-row scales
+    qws = torch.empty(256, dtype=torch.uint8, device=dev)
+    qt = []
+    for _ in range(6):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(torch.cuda.current_stream())
+        mtp.mtp_quantize_head_fp8(dw.tensors["lm_head"], V, H, q, s, qws)
+        e1.record(torch.cuda.current_stream())
+        torch.cuda.synchronize()
+        qt.append(e0.elapsed_time(e1) * 1e3)
+    q_us = float(np.median(qt[1:]))
+    q_bytes = V * H * 3 + 4 * V
+    quant = {"call_us": round(q_us, 1), "call_GBps": round(q_bytes / q_us / 1e3, 1),
+             "call_frac_of_peak": round(q_bytes / q_us / 1e3 / HBM_PEAK_GBPS, 4),
+             "bytes": q_bytes, "note": "median of 5 calls after one warm-up, HIP events around "
+             "the whole call: the flag clear, the quantise kernel, and the synchronising read "
+             "of the non-finite flag (the kernel alone is in the rocprofv3 trace)"}
+    print(f"[bench] quantiser: {quant}", file=sys.stderr, flush=True)
+
     tk = torch.from_numpy(tokens.astype(np.uint32).view(np.int32)).to(dev)
     hd = harness.to_dev_bf16(hidden)
     draft = torch.empty(B, dtype=torch.int32, device=dev)
@@ -164,6 +185,47 @@ def main():
     mtp.mtp_front(dw.w, B, tk, hd, x, ws, stream)
     torch.cuda.synchronize()
 
+    # three copies of eh_proj (3 x 151 MB at the Large shape, more than the
+    # 256 MB last-level cache), used in turn by the cold-front sweeps and the
+    # context rows, so those calls stream eh_proj from HBM
+    t = dw.tensors
+    cw = [dw.w] + [mtp.mtp_weights(t["embed"], t["enorm_w"], t["hnorm_w"], t["head_norm_w"],
+                                   t["eh_proj"].clone(), t["lm_head"], float(wts["rms_eps"]))
+                   for _ in range(2)]
+
+    def spread(fn, blocks=20, per=10):
+        """Per-call µs from HIP events around blocks of back-to-back calls:
+        p10, median, p90 over the blocks."""
+        for _ in range(per):
+            fn()
+        vals = []
+        for _ in range(blocks):
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for _ in range(per):
+                fn()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            vals.append(e0.elapsed_time(e1) * 1e3 / per)
+        p10, med, p90 = np.percentile(vals, [10, 50, 90])
+        return {"p10_us": round(float(p10), 2), "median_us": round(float(med), 2),
+                "p90_us": round(float(p90), 2), "blocks": blocks, "calls_per_block": per}
+
+    def synced(fn, n=100):
+        """Host latency of one call that is waited for and whose draft is read
+        back (4 bytes), as a caller that needs the token at once sees it."""
+        for _ in range(5):
+            fn()
+            draft.cpu()
+        vals = []
+        for _ in range(n):
+            t1 = time.perf_counter()
+            fn()
+            draft.cpu()
+            vals.append((time.perf_counter() - t1) * 1e6)
+        return round(float(np.median(vals)), 2)
+
     res = {}
     for name, fp8 in (("bf16", False), ("fp8", True)):
         gpu_s, wall_s = timed(lambda: sweep(fp8), args.steps, args.warmup)
@@ -179,6 +241,22 @@ def main():
             "lm_head_GBps": gbps,
             "lm_head_frac_of_peak": gbps / HBM_PEAK_GBPS,
             "sweep_GBps": sweep_bytes(H, V, B, fp8) / (gpu_s / args.steps) / 1e9,
+        }
+        turn = [0]
+
+        def cold(fp8=fp8):
+            turn[0] = (turn[0] + 1) % len(cw)
+            if fp8:
+                mtp.mtp_draft_fp8w(cw[turn[0]], q, s, B, tk, hd, draft, logits, ws, stream)
+            else:
+                mtp.mtp_draft_bf16(cw[turn[0]], B, tk, hd, draft, logits, ws, stream)
+        cold_s, cold_wall = timed(cold, args.steps, args.warmup)
+        res[name]["detail"] = {
+            "sweep_per_call": spread(lambda: sweep(fp8)),
+            "head_per_call": spread(lambda: head(fp8)),
+            "sync_each_call_us": synced(lambda: sweep(fp8)),
+            "cold_eh_proj_sweeps_per_s": round(args.steps / cold_wall, 2),
+            "cold_eh_proj_ms_per_step": round(cold_wall / args.steps * 1e3, 5),
         }
         print(f"[bench] {name}: {res[name]}", file=sys.stderr, flush=True)
 
@@ -246,12 +324,6 @@ def main():
         cx = torch.empty((Tmax, H), dtype=torch.bfloat16, device=dev)
         cws = torch.empty(mtp.mtp_context_workspace_bytes(H, Tmax), dtype=torch.uint8,
                           device=dev)
-        # three copies of eh_proj (3 x 151 MB, more than the 256 MB last-level
-        # cache), used in turn, so that every call streams it from HBM
-        t = dw.tensors
-        cw = [dw.w] + [mtp.mtp_weights(t["embed"], t["enorm_w"], t["hnorm_w"], t["head_norm_w"],
-                                       t["eh_proj"].clone(), t["lm_head"], float(wts["rms_eps"]))
-                       for _ in range(2)]
         turn = [0]
 
         def ctx_call(T):
@@ -370,7 +442,9 @@ def main():
                         "frac_of_peak": round(v["lm_head_frac_of_peak"], 4),
                         "head_us": round(v["head_us"], 2),
                         "sweeps_per_s": round(v["sweeps_per_s"], 2),
-                        "ms_per_step": round(v["ms_per_step"], 5)} for k, v in res.items()},
+                        "ms_per_step": round(v["ms_per_step"], 5),
+                        **v["detail"]} for k, v in res.items()},
+        "fp8_quantiser": quant,
         "batched": batched,
         "chained_drafts": chain,
         "context_rows": context,
