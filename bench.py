@@ -98,6 +98,16 @@ def sweep_bytes(H: int, V: int, B: int, fp8: bool) -> int:
     return 2 * H * H * 2 + head_bytes(H, V, B, fp8) + B * 2 * H * 2 + 2 * H * 2
 
 
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -422,6 +432,39 @@ def main():
                "kind": "oracle",
                "sample": f"{n} full {cfg.name} BF16 draft sweep(s) (B={B}) through the FP64 "
                          f"oracle, {el:.1f}s, {nthreads} threads splitting vocab rows"}
+        # the same oracle on one thread, the FP8 head path, and the quantiser;
+        # the one-thread figures time row samples of the same matrices and
+        # scale them to the whole sweep (every row costs the same)
+        detail = {"cpu_model": cpu_model()}
+        tq = time.perf_counter()
+        q_or, s_or = oracle.quantize_fp8(wts["lm_head"], nthreads=nthreads)
+        detail["quantiser_s"] = round(time.perf_counter() - tq, 3)
+        detail["quantiser_threads"] = nthreads
+        n8, t_end = 0, time.perf_counter() + 3.0
+        tc = time.perf_counter()
+        while True:
+            for b in range(B):
+                oracle.draft(wts, int(tokens[b]), hidden[b], fp8=(q_or, s_or), nthreads=nthreads)
+            n8 += 1
+            if time.perf_counter() >= t_end:
+                break
+        detail["fp8_sweeps_per_s"] = round(n8 / (time.perf_counter() - tc), 4)
+        rows = min(V, 16384)
+        xs = synth.to_bf16(np.ones(H, np.float32))
+        cs = synth.to_bf16(np.ones(2 * H, np.float32))
+        t1 = time.perf_counter()
+        oracle.gemv_bf16(wts["eh_proj"], cs, nthreads=1)
+        t_front = time.perf_counter() - t1
+        t1 = time.perf_counter()
+        oracle.gemv_bf16(wts["lm_head"][:rows], xs, nthreads=1)
+        t_head = (time.perf_counter() - t1) * V / rows
+        detail["bf16_sweeps_per_s_1thread"] = round(1.0 / (t_front + t_head), 4)
+        t1 = time.perf_counter()
+        oracle.quantize_fp8(wts["lm_head"][:rows // 4], nthreads=1)
+        detail["quantiser_s_1thread"] = round((time.perf_counter() - t1) * V / (rows // 4), 3)
+        detail["one_thread_sample"] = (f"eh_proj GEMV whole, lm_head GEMV over {rows} rows and "
+                                       f"the quantiser over {rows // 4} rows, scaled to {V} rows")
+        cpu["detail"] = detail
 
     line = {
         "metric": METRIC,
