@@ -47,6 +47,8 @@ def parse():
                    help="skip the chained-draft (K = 4 drafts per call) timings")
     p.add_argument("--no-context", action="store_true",
                    help="skip the context-row (prompt / catch-up rows) timings")
+    p.add_argument("--no-shards", action="store_true",
+                   help="skip the head timings at vocabulary-shard shapes (V/2, V/4, V/8 rows)")
     p.add_argument("--no-agreement", action="store_true",
                    help="skip the BF16-vs-FP8 draft agreement study")
     p.add_argument("--calib-copy", action="store_true",
@@ -270,6 +272,37 @@ def main():
         }
         print(f"[bench] {name}: {res[name]}", file=sys.stderr, flush=True)
 
+    # The per-GPU kernel of a vocabulary-sharded head (the pages' TP sweep):
+    # the head over the first V/G rows, what one of G GPUs would sweep before
+    # the cross-GPU pick.  Only the kernel is timed here; the exchange of the
+    # per-shard (max, index) is not built.
+    shards = None
+    if not args.no_shards:
+        shards = {}
+        t = dw.tensors
+        for G in (2, 4, 8):
+            Vs = V // G
+            # the first Vs rows of each [V][H] table (the head reads no embedding)
+            sw = mtp.mtp_weights(t["embed"][:Vs], t["enorm_w"], t["hnorm_w"], t["head_norm_w"],
+                                 t["eh_proj"], t["lm_head"][:Vs], float(wts["rms_eps"]))
+            slg = logits[:, :Vs]
+            sws = mtp.new_workspace(H, Vs, B)
+            ent = {"rows": Vs}
+            for name, fp8 in (("bf16", False), ("fp8", True)):
+                def shead():
+                    if fp8:
+                        mtp.mtp_head_fp8w(sw, q[:Vs], s[:Vs], B, x, draft, slg, sws, stream)
+                    else:
+                        mtp.mtp_head_bf16(sw, B, x, draft, slg, sws, stream)
+                g_s, _ = timed(shead, args.steps, args.warmup)
+                per = g_s / args.steps
+                ent[name] = {"head_us": round(per * 1e6, 2),
+                             "GBps": round(head_bytes(H, Vs, B, fp8) / per / 1e9, 1),
+                             "frac_of_peak": round(head_bytes(H, Vs, B, fp8) / per / 1e9
+                                                   / HBM_PEAK_GBPS, 4)}
+            shards[f"G{G}"] = ent
+        print(f"[bench] vocab shards: {shards}", file=sys.stderr, flush=True)
+
     batched = None
     if not args.no_batched and args.config == "large":
         batched = {}
@@ -488,6 +521,7 @@ def main():
                         "ms_per_step": round(v["ms_per_step"], 5),
                         **v["detail"]} for k, v in res.items()},
         "fp8_quantiser": quant,
+        "vocab_shard_heads": shards,
         "batched": batched,
         "chained_drafts": chain,
         "context_rows": context,
