@@ -35,28 +35,56 @@ __global__ __launch_bounds__(512) void sum_norm_kernel(SumNormArgs a)
         single_norm(a.x_in + size_t(b) * H, a.norm_w, H, a.eps, a.xn_out + size_t(b) * H, red);
         return;
     }
-    // x = BF16(sum_s P[s][b]) in split order; every load (the partial sums and
-    // the norm weights) is issued before the first add
+    // x = BF16(sum_s P[s][b]) in split order.  The partial sums are loaded
+    // eight splits at a time for both pieces (a split past S re-reads the
+    // last one and is not added), all issued before the first add, so a batch
+    // of splits costs one memory latency rather than one per split.
     uint4 v[2], wv[2];
+    float acc[2][8];
+    bool in[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const int j = (i * blockDim.x + tid) * 8;
+        in[i] = j < H;
+        wv[i] = make_uint4(0, 0, 0, 0);
+        if (in[i] && a.xn_out)
+            wv[i] = *reinterpret_cast<const uint4 *>(a.norm_w + j);
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+            acc[i][e] = 0.f;
+    }
+    for (int sp0 = 0; sp0 < a.S; sp0 += 8) {
+        float4 p[2][8][2];
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            // a piece past H reads piece 0 of the row (never added)
+            const int j = in[i] ? (i * blockDim.x + tid) * 8 : 0;
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const int sp = min(sp0 + u, a.S - 1);
+                const float *src = a.P + (size_t(sp) * a.B + b) * H + j;
+                p[i][u][0] = *reinterpret_cast<const float4 *>(src);
+                p[i][u][1] = *reinterpret_cast<const float4 *>(src + 4);
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+            for (int u = 0; u < 8; ++u)
+                if (sp0 + u < a.S) {
+                    acc[i][0] += p[i][u][0].x; acc[i][1] += p[i][u][0].y;
+                    acc[i][2] += p[i][u][0].z; acc[i][3] += p[i][u][0].w;
+                    acc[i][4] += p[i][u][1].x; acc[i][5] += p[i][u][1].y;
+                    acc[i][6] += p[i][u][1].z; acc[i][7] += p[i][u][1].w;
+                }
+    }
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
         const int j = (i * blockDim.x + tid) * 8;
         v[i] = make_uint4(0, 0, 0, 0);
-        wv[i] = make_uint4(0, 0, 0, 0);
-        if (j < H && a.xn_out)
-            wv[i] = *reinterpret_cast<const uint4 *>(a.norm_w + j);
-        if (j < H) {
-            float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-#pragma unroll 8
-            for (int sp = 0; sp < a.S; ++sp) {
-                const float *src = a.P + (size_t(sp) * a.B + b) * H + j;
-                const float4 p0 = *reinterpret_cast<const float4 *>(src);
-                const float4 p1 = *reinterpret_cast<const float4 *>(src + 4);
-                acc[0] += p0.x; acc[1] += p0.y; acc[2] += p0.z; acc[3] += p0.w;
-                acc[4] += p1.x; acc[5] += p1.y; acc[6] += p1.z; acc[7] += p1.w;
-            }
-            v[i] = make_uint4(pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3]),
-                              pack_bf16x2(acc[4], acc[5]), pack_bf16x2(acc[6], acc[7]));
+        if (in[i]) {
+            v[i] = make_uint4(pack_bf16x2(acc[i][0], acc[i][1]), pack_bf16x2(acc[i][2], acc[i][3]),
+                              pack_bf16x2(acc[i][4], acc[i][5]), pack_bf16x2(acc[i][6], acc[i][7]));
             if (a.x_out)
                 *reinterpret_cast<uint4 *>(a.x_out + size_t(b) * H + j) = v[i];
         }
