@@ -307,16 +307,27 @@ __global__ __launch_bounds__(256) void argmax_final_kernel(const Partial *__rest
     __shared__ uint32_t si[4];
     const int b = blockIdx.x;
     const int tid = threadIdx.x;
-    // the token check's load goes out together with the partials' loads
-    const bool invalid = tokens && tid == 0 && tokens[b] >= uint32_t(vocab);
+    // the token check's load (every lane reads the same word) goes out
+    // together with the partials' loads and is used only at the end
+    const uint32_t tk = tokens ? tokens[b] : 0u;
     float bv = -INFINITY;
     uint32_t bi = 0xFFFFFFFFu;
-    for (int p = tid; p < nparts; p += blockDim.x) {
-        const Partial q = partials[size_t(b) * kMaxHeadBlocks + p];
-        if (better(q.val, q.idx, bv, bi)) {
-            bv = q.val;
-            bi = q.idx;
-        }
+    // four partials per thread are loaded before any is compared (one memory
+    // latency per batch, not per partial); a slot past nparts re-reads the
+    // last partial and is skipped.  The (value, lower index) order is
+    // associative, so the batching does not change the result.
+    constexpr int PER = 4;
+    for (int p0 = tid; p0 < nparts; p0 += PER * int(blockDim.x)) {
+        Partial q[PER];
+#pragma unroll
+        for (int u = 0; u < PER; ++u)
+            q[u] = partials[size_t(b) * kMaxHeadBlocks + min(p0 + u * int(blockDim.x), nparts - 1)];
+#pragma unroll
+        for (int u = 0; u < PER; ++u)
+            if (p0 + u * int(blockDim.x) < nparts && better(q[u].val, q[u].idx, bv, bi)) {
+                bv = q[u].val;
+                bi = q[u].idx;
+            }
     }
     wave_argmax(bv, bi);
     if ((tid & (kWave - 1)) == 0) {
@@ -331,7 +342,7 @@ __global__ __launch_bounds__(256) void argmax_final_kernel(const Partial *__rest
                 bv = sv[w];
                 bi = si[w];
             }
-        if (invalid)
+        if (tokens && tk >= uint32_t(vocab))
             bi = 0xFFFFFFFFu;
         draft[b] = bi;
     }
