@@ -49,6 +49,8 @@ def parse():
                    help="skip the context-row (prompt / catch-up rows) timings")
     p.add_argument("--no-shards", action="store_true",
                    help="skip the head timings at vocabulary-shard shapes (V/2, V/4, V/8 rows)")
+    p.add_argument("--no-ceiling", action="store_true",
+                   help="skip the plain streaming-read probe (the practical HBM ceiling)")
     p.add_argument("--no-agreement", action="store_true",
                    help="skip the BF16-vs-FP8 draft agreement study")
     p.add_argument("--calib-copy", action="store_true",
@@ -428,6 +430,29 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
+    # The practical ceiling: a plain streaming read of the same lm_head bytes
+    # (16-byte non-temporal loads, nothing computed), best over grid sizes.
+    ceiling = None
+    if not args.no_ceiling:
+        pout = torch.zeros(1, dtype=torch.int32, device=dev)
+        lmh = dw.tensors["lm_head"]
+        nb = lmh.numel() * lmh.element_size()
+        best = None
+        per = {}
+        for per_cu in (1, 2, 4, 8):
+            g_s, _ = timed(lambda: mtp.mtp_probe_stream_read(lmh, pout, per_cu, stream),
+                           max(20, args.steps // 4), 5)
+            gbps = nb / (g_s / max(20, args.steps // 4)) / 1e9
+            per[f"wg_per_cu_{per_cu}"] = round(gbps, 1)
+            if best is None or gbps > best[0]:
+                best = (gbps, per_cu)
+        ceiling = {"GBps": round(best[0], 1), "frac_of_peak": round(best[0] / HBM_PEAK_GBPS, 4),
+                   "wg_per_cu": best[1], "by_grid": per,
+                   "buffer": f"the BF16 lm_head, {nb} bytes",
+                   "lm_head_bf16_frac_of_ceiling": round(res["bf16"]["lm_head_GBps"] / best[0], 4),
+                   "lm_head_fp8_frac_of_ceiling": round(res["fp8"]["lm_head_GBps"] / best[0], 4)}
+        print(f"[bench] streaming-read ceiling: {ceiling}", file=sys.stderr, flush=True)
+
     main_path = "bf16"
     r = res[main_path]
     hb = head_bytes(H, V, B, False)
@@ -526,6 +551,7 @@ def main():
         "chained_drafts": chain,
         "context_rows": context,
         "draft_agreement_fp8_vs_bf16": agreement,
+        "streaming_read_ceiling": ceiling,
         "roofline": roof,
         "cpu_baseline": cpu,
     }

@@ -21,7 +21,7 @@ __all__ = [
     "lib", "lib_path", "mtp_workspace_bytes", "mtp_validate_draft_args",
     "mtp_quantize_head_fp8", "mtp_draft_bf16", "mtp_draft_fp8w", "mtp_front", "mtp_head_bf16",
     "mtp_head_fp8w", "mtp_status_str", "new_workspace", "mtp_context_workspace_bytes",
-    "mtp_context_rows",
+    "mtp_context_rows", "mtp_probe_stream_read",
 ]
 
 MTP_OK, MTP_ERR_NULL, MTP_ERR_SHAPE, MTP_ERR_ALIGN = 0, 1, 2, 3
@@ -80,6 +80,7 @@ def lib():
             "mtp_chain_workspace_bytes": ([i32, i32, i32], sz),
             "mtp_draft_chain_bf16": ([W, i32, i32, P, P, P, P, P, sz, P], ctypes.c_int),
             "mtp_draft_chain_fp8w": ([W, P, P, i32, i32, P, P, P, P, P, sz, P], ctypes.c_int),
+            "mtp_probe_stream_read": ([P, sz, P, i32, P], ctypes.c_int),
         }
         for name, (args, res) in sigs.items():
             f = getattr(L, name)
@@ -308,3 +309,16 @@ def mtp_draft_chain_fp8w(w: mtp_weights, q, scale, steps: int, batch: int, token
                                       _dev(scale, "scale", torch.float32, w.vocab), steps, batch,
                                       t, h, d, lg, ws, nws, _stream(stream)),
            "mtp_draft_chain_fp8w")
+
+
+def mtp_probe_stream_read(buf, out, wg_per_cu: int = 2, stream=None) -> None:
+    """A plain streaming read of the device tensor `buf` (a measurement aid:
+    the practical HBM ceiling the weight sweeps are compared with).  `out` is
+    a device int32/uint32 tensor of at least one element."""
+    if not isinstance(buf, torch.Tensor) or not buf.is_cuda or not buf.is_contiguous():
+        raise ValueError("buf must be a contiguous device tensor")
+    nbytes = buf.numel() * buf.element_size()
+    o = (_dev(out, "out", torch.int32, 1) if out.dtype == torch.int32
+         else _dev(out, "out", torch.uint32, 1))
+    _check(lib().mtp_probe_stream_read(ctypes.c_void_p(buf.data_ptr()), nbytes, o,
+                                       int(wg_per_cu), _stream(stream)), "mtp_probe_stream_read")

@@ -12,12 +12,16 @@ import mtp_draft_head_embed_amd as mtp
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "mtp_draft.h")
+HEADERS = sorted(os.path.join(ROOT, "include", f) for f in os.listdir(os.path.join(ROOT, "include"))
+                 if f.endswith(".h"))
 
 
 def declared_functions():
-    text = open(HEADER).read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(mtp_[a-z0-9_]+)\s*\(", text)))
+    names = set()
+    for h in HEADERS:
+        text = re.sub(r"/\*.*?\*/", "", open(h).read(), flags=re.S)
+        names.update(re.findall(r"\b(mtp_[a-z0-9_]+)\s*\(", text))
+    return sorted(names)
 
 
 def test_header_symbols_exported():
@@ -144,3 +148,18 @@ def test_chain_workspace_and_validation():
     assert L.mtp_draft_chain_fp8w(ctypes.byref(w), None, P(0x80000), 3, B, P(0x90000),
                                   P(0xA0000), P(0xB0000), None, P(0xD0000), ch,
                                   None) == mtp.MTP_ERR_NULL
+
+
+def test_probe_argument_errors():
+    """The streaming-read probe rejects bad arguments on the host, before any
+    launch."""
+    L = mtp.lib()
+    P = ctypes.c_void_p
+    assert L.mtp_probe_stream_read(None, 1024, P(0x1000), 2, None) == mtp.MTP_ERR_NULL
+    assert L.mtp_probe_stream_read(P(0x1000), 1024, None, 2, None) == mtp.MTP_ERR_NULL
+    assert L.mtp_probe_stream_read(P(0x1000), 0, P(0x2000), 2, None) == mtp.MTP_ERR_SHAPE
+    assert L.mtp_probe_stream_read(P(0x1000), 1000, P(0x2000), 2, None) == mtp.MTP_ERR_SHAPE
+    assert L.mtp_probe_stream_read(P(0x1000), 1024, P(0x2000), 0, None) == mtp.MTP_ERR_SHAPE
+    assert L.mtp_probe_stream_read(P(0x1000), 1024, P(0x2000), 17, None) == mtp.MTP_ERR_SHAPE
+    assert L.mtp_probe_stream_read(P(0x1008), 1024, P(0x2000), 2, None) == mtp.MTP_ERR_ALIGN
+    assert L.mtp_probe_stream_read(P(0x1000), 1024, P(0x2002), 2, None) == mtp.MTP_ERR_ALIGN

@@ -151,6 +151,18 @@ def test_quantiser_midpoint_quotients():
     assert np.array_equal(sg.view(np.uint32), ref[1].view(np.uint32))
 
 
+def test_stream_read_probe():
+    """The streaming-read probe (a measurement aid) runs over a ragged-size
+    buffer and leaves its output alone when the folded words do not match."""
+    import mtp_draft_head_embed_amd as mtp
+    buf = torch.zeros((1 << 20) + 48, dtype=torch.uint8, device="cuda")
+    out = torch.full((1,), 7, dtype=torch.int32, device="cuda")
+    for per_cu in (1, 2, 16):
+        mtp.mtp_probe_stream_read(buf, out, per_cu)
+    torch.cuda.synchronize()
+    assert int(out.item()) == 7
+
+
 def test_quantiser_nonfinite():
     import mtp_draft_head_embed_amd as mtp
     for bad in (0x7F80, 0xFF80, 0x7FC0):
