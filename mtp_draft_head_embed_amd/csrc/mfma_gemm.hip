@@ -129,7 +129,7 @@ __global__ __launch_bounds__(WPB * 64) void mfma_gemm_kernel(MfmaArgs a)
     // are issued before any of them is stored, so the chunk costs about one
     // memory latency rather than one per load.
     auto stage = [&](int kc0) {
-        constexpr int SB = 8;
+        constexpr int SB = NBT >= 3 ? 8 : 16;  // fewer where the batch tiles hold many registers
         const int kc_len = min(KC, k_end - kc0);
         const int n16 = B * (KC / 8);
         for (int i0 = tid; i0 < n16; i0 += SB * NT) {
