@@ -14,12 +14,18 @@
 //     for a few dozen (more weight rows staged per step); every wave owns a
 //     64 x 64, 64 x 48 or 64 x 32 block of v_mfma_f32_16x16x32_bf16
 //     accumulators;
-//   * K in steps of 32 columns through four LDS stages, each its own LDS
-//     object; the operands go from HBM straight into LDS (buffer loads with
-//     the LDS flag: no registers, no LDS store instructions), issued three
-//     steps ahead, so a step waits only for the loads of the step after it;
-//   * a staged row is 64 bytes; 16-byte piece c of row r sits at slot
-//     c ^ ((r >> 1) & 3), so the 16-lane fragment reads hit distinct banks;
+//   * K in steps through four LDS stages, each its own LDS object; the
+//     operands go from HBM straight into LDS (buffer loads with the LDS flag:
+//     no registers, no LDS store instructions), issued three steps ahead, so
+//     a step waits only for the loads of the step after it;
+//   * a step is 32 columns (a 64-byte staged row, 16 rows per load
+//     instruction) for the large tiles, and 64 columns (128-byte rows, 8 rows
+//     per load instruction) for the two skinny tiles, whose time goes to
+//     streaming eh_proj: each load then reads 128 contiguous bytes of a
+//     weight row, which streams faster than 64 (one workgroup per CU then
+//     fits in LDS);
+//   * 16-byte piece c of staged row r sits at slot c ^ ((r >> 1) & (n - 1))
+//     for n pieces per row, so the 16-lane fragment reads hit distinct banks;
 //   * the fragment reads are plain ds_read_b128 the compiler does not see as
 //     LDS accesses, with explicit waits that the MFMAs depend on: otherwise
 //     it waits for every load in flight before each read (it cannot tell
@@ -46,10 +52,15 @@ typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void lds_void_t;
 
-constexpr int BK = 32;      // K columns per step
-constexpr int RB = BK * 2;  // bytes per staged row
-
-__device__ __forceinline__ int slot(int row, int piece) { return piece ^ ((row >> 1) & 3); }
+// Slot of 16-byte piece `piece` of staged row `row` when a staged row holds
+// NP pieces (NP = 4: 64 bytes, 32 columns; NP = 8: 128 bytes, 64 columns):
+// rows of the same parity start at the same bank, and the XOR spreads the
+// 16 rows of a fragment read over distinct 16-byte bank groups.
+template <int NP>
+__host__ __device__ __forceinline__ int slot(int row, int piece)
+{
+    return piece ^ ((row >> 1) & (NP - 1));
+}
 
 __device__ __forceinline__ bf16x8_t as_bf16x8(const u32x4_t &u)
 {
@@ -65,29 +76,35 @@ __device__ __forceinline__ uint32_t lds_offset(const void *p)
 
 }  // namespace
 
-template <int BM, int BN, int WM, int WN>
+template <int BM, int BN, int WM, int WN, int BK = 32>
 __global__ __launch_bounds__(WM *WN * 64) void ctx_gemm_kernel(const uint16_t *__restrict__ A,
                                                                const uint16_t *__restrict__ W,
                                                                uint16_t *__restrict__ C,
                                                                float *__restrict__ P, int M, int N,
                                                                int K, int Ks)
 {
+    // BK columns per step: each staged row holds RB = 2 BK bytes in NP pieces
+    // of 16, and one load instruction stages RPL = 64 / NP rows
+    static_assert(BK == 32 || BK == 64, "steps of 32 or 64 columns");
+    constexpr int RB = BK * 2, NP = RB / 16, RPL = 64 / NP, NSUB = BK / 32;
     constexpr int NW = WM * WN;
     constexpr int FM = BM / WM / 16, FN = BN / WN / 16;
     static_assert(FM == 4, "the staged waits below assume four A fragments per wave");
     static_assert(FN >= 2 && FN <= 4, "two to four W fragments per wave");
-    // A load instruction stages 16 rows.  The A rows go to the waves in equal
-    // contiguous shares; so do the W rows when they divide evenly, else W row
-    // group q (16 rows) goes to wave q, and the waves past the last group
-    // stage nothing real: their load reads past the resource (zeros) into a
-    // 1 KiB slot past the stage, so every wave issues the same number of
-    // loads per step and the vmcnt waits below hold for all of them.
+    // A load instruction stages RPL rows (16 of 64 bytes or 8 of 128).  The A
+    // rows go to the waves in equal contiguous shares; so do the W rows when
+    // they divide evenly, else W row group q (16 rows) goes to wave q, and the
+    // waves past the last group stage nothing real: their load reads past the
+    // resource (zeros) into a 1 KiB slot past the stage, so every wave issues
+    // the same number of loads per step and the vmcnt waits below hold for
+    // all of them.
     constexpr int RA = BM / NW;
-    static_assert(RA % 16 == 0 && BN % 16 == 0, "a load instruction stages 16 rows");
+    static_assert(RA % 16 == 0 && BN % 16 == 0, "waves stage whole 16-row groups");
     constexpr bool WSPLIT = (BN / NW) % 16 == 0;
     static_assert(WSPLIT || BN / 16 <= NW, "uneven W staging takes one group per wave");
+    static_assert(WSPLIT || BK == 32, "uneven W staging is laid out for 64-byte rows");
     constexpr int RW = WSPLIT ? BN / NW : 16;
-    constexpr int IA = RA / 16, IW = RW / 16;
+    constexpr int IA = RA / RPL, IW = RW / RPL;
     constexpr int STAGE = (BM + BN) * RB + (WSPLIT ? 0 : (NW - BN / 16) * 16 * RB);
     // two newer stages may stay in flight when a step's stage must be in
     constexpr int INFLIGHT = 2 * (IA + IW);
@@ -125,42 +142,47 @@ __global__ __launch_bounds__(WM *WN * 64) void ctx_gemm_kernel(const uint16_t *_
     const __amdgpu_buffer_rsrc_t wrsrc = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<uint16_t *>(W) + size_t(n0) * K, 0, int(uint32_t(min(BN, N - n0)) * rowb),
         0x00020000);
-    // A load instruction stages 16 rows: lane L takes row L/4 and LDS slot L%4,
-    // which holds piece (L%4) ^ ((row >> 1) & 3) of the row's 64 bytes.
-    const int lrow = lane >> 2;
-    const int lpiece = (lane & 3) ^ ((lrow >> 1) & 3);
-    const uint32_t lofs = uint32_t(lrow) * rowb + uint32_t(lpiece) * 16;
+    // A load instruction stages RPL rows from row r0 on: lane L takes row
+    // r0 + L / NP and LDS slot L % NP, which holds piece slot<NP>(row, L % NP)
+    // of the row's RB bytes (the XOR is its own inverse, and it depends on
+    // the row within its 16-row group, as the fragment reads below do).
+    const int lrow = lane / NP, lslot = lane % NP;
+    // A piece past the split reads zero (an offset past the range): K and
+    // the split bounds are multiples of 32 columns, so a 64-column step can
+    // end half past the split, and must not read the next row's first columns.
     auto issue = [&](char *st, int k0) {
-        // a step lies wholly inside or wholly past the split (both multiples of 32)
-        const uint32_t o = k0 < k_end ? lofs + uint32_t(k0) * 2 : 0x80000000u;
 #pragma unroll
-        for (int j = 0; j < IA; ++j) {
-            const int r0 = wid * RA + 16 * j;
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(arsrc, (lds_void_t *)(st + r0 * RB), 16,
-                                                     o + uint32_t(r0) * rowb, 0, 0, 0);
-        }
-#pragma unroll
-        for (int j = 0; j < IW; ++j) {
-            const int r0 = wid * RW + 16 * j;
+        for (int j = 0; j < IA + IW; ++j) {
+            const bool is_a = j < IA;
+            const int r0 = is_a ? wid * RA + RPL * j : wid * RW + RPL * (j - IA);
+            const int pc = slot<NP>(r0 + lrow, lslot);
             // uneven W staging: a wave past the last group fills its own slot
             // after the stage's W rows with zeros (an offset past the range)
-            const uint32_t ow = (WSPLIT || r0 < BN) ? o + uint32_t(r0) * rowb : 0x80000000u;
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(wrsrc, (lds_void_t *)(st + BM * RB + r0 * RB),
-                                                     16, ow, 0, 0, 0);
+            const bool live = k0 + pc * 8 < k_end && (is_a || WSPLIT || r0 < BN);
+            const uint32_t off = live ? uint32_t(r0 + lrow) * rowb + uint32_t(pc) * 16 +
+                                            uint32_t(k0) * 2
+                                      : 0x80000000u;
+            char *dst = is_a ? st + r0 * RB : st + BM * RB + r0 * RB;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(is_a ? arsrc : wrsrc, (lds_void_t *)dst, 16,
+                                                     off, 0, 0, 0);
         }
     };
 
-    // fragment addresses inside a stage: lane (g, n) reads row n, piece g
-    uint32_t aoff[FM], woff[FN];
+    // fragment addresses inside a stage: for the 32 columns of sub-step u,
+    // lane (g, n) reads row n, piece 4u + g
+    uint32_t aoff[NSUB][FM], woff[NSUB][FN];
 #pragma unroll
-    for (int i = 0; i < FM; ++i) {
-        const int row = (wm * FM + i) * 16 + nl;
-        aoff[i] = uint32_t(row * RB + slot(row, g) * 16);
-    }
+    for (int u = 0; u < NSUB; ++u) {
 #pragma unroll
-    for (int j = 0; j < FN; ++j) {
-        const int row = (wn * FN + j) * 16 + nl;
-        woff[j] = uint32_t(BM * RB + row * RB + slot(row, g) * 16);
+        for (int i = 0; i < FM; ++i) {
+            const int row = (wm * FM + i) * 16 + nl;
+            aoff[u][i] = uint32_t(row * RB + slot<NP>(row, 4 * u + g) * 16);
+        }
+#pragma unroll
+        for (int j = 0; j < FN; ++j) {
+            const int row = (wn * FN + j) * 16 + nl;
+            woff[u][j] = uint32_t(BM * RB + row * RB + slot<NP>(row, 4 * u + g) * 16);
+        }
     }
 
     f32x4_t acc[FM][FN];
@@ -177,15 +199,16 @@ __global__ __launch_bounds__(WM *WN * 64) void ctx_gemm_kernel(const uint16_t *_
             acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a), as_bf16x8(w[j]),
                                                                 acc[i][j], 0, 0, 0);
     };
-    auto compute = [&](const char *st) {
+    // one sub-step: 32 columns of the stage, in k order
+    auto compute_sub = [&](const char *st, const uint32_t(&ao)[FM], const uint32_t(&wo)[FN]) {
         const uint32_t base = lds_offset(st);
         u32x4_t a[FM], w[FN];
 #pragma unroll
         for (int j = 0; j < FN; ++j)
-            asm volatile("ds_read_b128 %0, %1" : "=v"(w[j]) : "v"(base + woff[j]));
+            asm volatile("ds_read_b128 %0, %1" : "=v"(w[j]) : "v"(base + wo[j]));
 #pragma unroll
         for (int i = 0; i < FM; ++i)
-            asm volatile("ds_read_b128 %0, %1" : "=v"(a[i]) : "v"(base + aoff[i]));
+            asm volatile("ds_read_b128 %0, %1" : "=v"(a[i]) : "v"(base + ao[i]));
         // W and A row i are in once at most 3 - i reads are outstanding
         if constexpr (FN == 4)
             asm volatile("s_waitcnt lgkmcnt(3)"
@@ -201,6 +224,11 @@ __global__ __launch_bounds__(WM *WN * 64) void ctx_gemm_kernel(const uint16_t *_
         mma_row(std::integral_constant<int, 2>{}, a[2], w);
         asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(a[3]));
         mma_row(std::integral_constant<int, 3>{}, a[3], w);
+    };
+    auto compute = [&](const char *st) {
+#pragma unroll
+        for (int u = 0; u < NSUB; ++u)
+            compute_sub(st, aoff[u], woff[u]);
     };
 
     using I0 = std::integral_constant<int, 0>;
@@ -254,18 +282,18 @@ __global__ __launch_bounds__(WM *WN * 64) void ctx_gemm_kernel(const uint16_t *_
         }
 }
 
-template <int BM, int BN, int WM, int WN>
+template <int BM, int BN, int WM, int WN, int BK = 32>
 hipError_t launch_ctx_tile(const uint16_t *A, const uint16_t *W, uint16_t *C, float *P, int M,
                            int N, int K, CtxSplit sp, hipStream_t s)
 {
     const dim3 grid((N + BN - 1) / BN, (M + BM - 1) / BM, sp.S);
-    hipLaunchKernelGGL((ctx_gemm_kernel<BM, BN, WM, WN>), grid, dim3(WM * WN * 64), 0, s, A, W, C,
-                       sp.S > 1 ? P : nullptr, M, N, K, sp.Ks);
+    hipLaunchKernelGGL((ctx_gemm_kernel<BM, BN, WM, WN, BK>), grid, dim3(WM * WN * 64), 0, s, A,
+                       W, C, sp.S > 1 ? P : nullptr, M, N, K, sp.Ks);
     return hipGetLastError();
 }
 
-// K split of one tile shape: at most `target` workgroups (256 for the large
-// tiles, one per CU; 512 for the others, two per CU), all in one round.
+// K split of one tile shape: at most `target` workgroups (256, one per CU),
+// all in one round.
 static CtxSplit split_for(int M, int N, int K, int tile, int tm, int tn, long target)
 {
     const long tiles = long((N + tn - 1) / tn) * long((M + tm - 1) / tm);
@@ -286,10 +314,12 @@ static CtxSplit split_for(int M, int N, int K, int tile, int tm, int tn, long ta
 
 CtxSplit ctx_split(int M, int N, int K)
 {
+    // the skinny tiles stage 64 columns per step (128 KiB or 160 KiB of LDS:
+    // one workgroup per CU)
     if (M < kCtxMidTileMinRows)
-        return split_for(M, N, K, kCtxTile64x256, 64, 256, 512);
+        return split_for(M, N, K, kCtxTile64x256, 64, 256, 256);
     if (M < kCtxBigTileMinRows)
-        return split_for(M, N, K, kCtxTile128x128, 128, 128, 512);
+        return split_for(M, N, K, kCtxTile128x128, 128, 128, 256);
     // 256 x 256 or 256 x 192, whichever finishes in less tile work: rounds
     // of 256 workgroups times the work of one workgroup (at H = 6144 the
     // 192-wide tile turns 192 or 384 workgroups into whole rounds of 256 or
@@ -312,9 +342,9 @@ hipError_t launch_ctx_gemm(const uint16_t *A, const uint16_t *W, uint16_t *C, fl
     case kCtxTile256x192:
         return launch_ctx_tile<256, 192, 4, 4>(A, W, C, P, M, N, K, sp, s);
     case kCtxTile128x128:
-        return launch_ctx_tile<128, 128, 2, 4>(A, W, C, P, M, N, K, sp, s);
+        return launch_ctx_tile<128, 128, 2, 4, 64>(A, W, C, P, M, N, K, sp, s);
     default:
-        return launch_ctx_tile<64, 256, 1, 4>(A, W, C, P, M, N, K, sp, s);
+        return launch_ctx_tile<64, 256, 1, 4, 64>(A, W, C, P, M, N, K, sp, s);
     }
 }
 
