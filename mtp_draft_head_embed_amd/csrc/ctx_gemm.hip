@@ -7,23 +7,20 @@
 // The page stops each row at the block's KV-cache write (out of scope here).
 // With T rows, eh_proj is a dense GEMM C[T][H] = A[T][2H] . W[H][2H]^T with
 // both operands K-contiguous, HBM-bound for a few hundred rows and bound by
-// the matrix cores beyond.  One kernel, four tile shapes:
+// the matrix cores beyond.  One kernel, three tile shapes:
 //   * 256 x 256 or 256 x 192 output tile per 16-wave workgroup (one per CU)
 //     for many rows (whichever fills the CUs in whole rounds), 128 x 128 per
-//     8-wave workgroup for a hundred or so, 64 x 256 per 4-wave workgroup
-//     for a few dozen (more weight rows staged per step); every wave owns a
-//     64 x 64, 64 x 48 or 64 x 32 block of v_mfma_f32_16x16x32_bf16
-//     accumulators;
+//     8-wave workgroup below 256 rows; every wave owns a 64 x 64, 64 x 48 or
+//     64 x 32 block of v_mfma_f32_16x16x32_bf16 accumulators;
 //   * K in steps through four LDS stages, each its own LDS object; the
 //     operands go from HBM straight into LDS (buffer loads with the LDS flag:
 //     no registers, no LDS store instructions), issued three steps ahead, so
 //     a step waits only for the loads of the step after it;
 //   * a step is 32 columns (a 64-byte staged row, 16 rows per load
 //     instruction) for the large tiles, and 64 columns (128-byte rows, 8 rows
-//     per load instruction) for the two skinny tiles, whose time goes to
-//     streaming eh_proj: each load then reads 128 contiguous bytes of a
-//     weight row, which streams faster than 64 (one workgroup per CU then
-//     fits in LDS);
+//     per load instruction) for the skinny tile, whose time goes to streaming
+//     eh_proj: each load then reads 128 contiguous bytes of a weight row,
+//     which streams faster than 64 (one workgroup per CU then fits in LDS);
 //   * 16-byte piece c of staged row r sits at slot c ^ ((r >> 1) & (n - 1))
 //     for n pieces per row, so the 16-lane fragment reads hit distinct banks;
 //   * the fragment reads are plain ds_read_b128 the compiler does not see as
@@ -314,10 +311,10 @@ static CtxSplit split_for(int M, int N, int K, int tile, int tm, int tn, long ta
 
 CtxSplit ctx_split(int M, int N, int K)
 {
-    // the skinny tiles stage 64 columns per step (128 KiB or 160 KiB of LDS:
-    // one workgroup per CU)
-    if (M < kCtxMidTileMinRows)
-        return split_for(M, N, K, kCtxTile64x256, 64, 256, 256);
+    // the skinny tile stages 64 columns per step (128 KiB of LDS: one
+    // workgroup per CU); from 17 to 64 rows half its A rows are past T and
+    // read zero, and it still streams eh_proj faster than a 64 x 256 tile
+    // (160 KiB per 4-wave workgroup) did
     if (M < kCtxBigTileMinRows)
         return split_for(M, N, K, kCtxTile128x128, 128, 128, 256);
     // 256 x 256 or 256 x 192, whichever finishes in less tile work: rounds
@@ -341,10 +338,8 @@ hipError_t launch_ctx_gemm(const uint16_t *A, const uint16_t *W, uint16_t *C, fl
         return launch_ctx_tile<256, 256, 4, 4>(A, W, C, P, M, N, K, sp, s);
     case kCtxTile256x192:
         return launch_ctx_tile<256, 192, 4, 4>(A, W, C, P, M, N, K, sp, s);
-    case kCtxTile128x128:
-        return launch_ctx_tile<128, 128, 2, 4, 64>(A, W, C, P, M, N, K, sp, s);
     default:
-        return launch_ctx_tile<64, 256, 1, 4, 64>(A, W, C, P, M, N, K, sp, s);
+        return launch_ctx_tile<128, 128, 2, 4, 64>(A, W, C, P, M, N, K, sp, s);
     }
 }
 

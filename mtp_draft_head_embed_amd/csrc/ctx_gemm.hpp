@@ -6,11 +6,11 @@
 
 namespace mtp {
 
-// Context rows: C[M][N] = BF16(A[M][K] . W[N][K]^T) on MFMA in one of four
+// Context rows: C[M][N] = BF16(A[M][K] . W[N][K]^T) on MFMA in one of three
 // tile shapes, with K split S ways (Ks columns each, a multiple of 128) when
 // the tiles alone would leave CUs idle; then the FP32 partials P[S][M][N] are
 // summed by launch_sum_norm.
-enum CtxTile { kCtxTile64x256 = 0, kCtxTile128x128 = 1, kCtxTile256x256 = 2, kCtxTile256x192 = 3 };
+enum CtxTile { kCtxTile128x128 = 1, kCtxTile256x256 = 2, kCtxTile256x192 = 3 };
 struct CtxSplit {
     int S, Ks;
     int tile;  // CtxTile
@@ -21,10 +21,8 @@ hipError_t launch_ctx_gemm(const uint16_t *A, const uint16_t *W, uint16_t *C, fl
 // Rows from which the context rows use the tiled GEMM instead of the batched
 // split-K sweep.
 constexpr int kCtxGemmMinRows = 17;
-// Rows from which the GEMM uses the 128 x 128 tile (below: 64 x 256, which
-// stages more weight rows per step when few activation rows are needed) and
-// the 256 x 256 or 256 x 192 tile (whichever fills the CUs in fewer rounds).
-constexpr int kCtxMidTileMinRows = 65;
+// Rows from which the GEMM uses the 256 x 256 or 256 x 192 tile (whichever
+// fills the CUs in fewer rounds) instead of 128 x 128.
 constexpr int kCtxBigTileMinRows = 256;
 
 }  // namespace mtp

@@ -4,9 +4,9 @@ oracle's FP64 rows: each element within the final rounding plus the FP32
 summation bound (a plain one-ulp bound fails where the sum nearly cancels),
 almost all bit-equal (tests/harness.py, `check_eh_proj_rows`).  Covers the
 single-row kernel, the batched split-K sweep (2..16 rows) and the tiled MFMA
-GEMM in all three tile shapes (64 x 256 for 17..64 rows, 128 x 128 to 255,
-256 x 256 beyond; split over K for few tiles, with ragged row, column and K
-tiles)."""
+GEMM in its tile shapes (128 x 128 with 64-column steps for 17..255 rows,
+256 x 256 or 256 x 192 beyond; split over K for few tiles, with ragged row,
+column and K tiles)."""
 import numpy as np
 import pytest
 import torch
