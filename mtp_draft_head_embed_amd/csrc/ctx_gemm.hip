@@ -10,7 +10,7 @@
 // the matrix cores beyond.  One kernel, three tile shapes:
 //   * 256 x 256 or 256 x 192 output tile per 16-wave workgroup (one per CU)
 //     for many rows (whichever fills the CUs in whole rounds), 128 x 128 per
-//     8-wave workgroup below 256 rows; every wave owns a 64 x 64, 64 x 48 or
+//     8-wave workgroup up to 128 rows; every wave owns a 64 x 64, 64 x 48 or
 //     64 x 32 block of v_mfma_f32_16x16x32_bf16 accumulators;
 //   * K in steps through four LDS stages, each its own LDS object; the
 //     operands go from HBM straight into LDS (buffer loads with the LDS flag:

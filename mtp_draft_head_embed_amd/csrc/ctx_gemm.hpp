@@ -22,7 +22,9 @@ hipError_t launch_ctx_gemm(const uint16_t *A, const uint16_t *W, uint16_t *C, fl
 // split-K sweep.
 constexpr int kCtxGemmMinRows = 17;
 // Rows from which the GEMM uses the 256 x 256 or 256 x 192 tile (whichever
-// fills the CUs in fewer rounds) instead of 128 x 128.
-constexpr int kCtxBigTileMinRows = 256;
+// fills the CUs in fewer rounds) instead of 128 x 128: the small tile is
+// faster while one row tile holds every row (eh_proj then streams once),
+// the large ones from the row count where the small tile would need two.
+constexpr int kCtxBigTileMinRows = 129;
 
 }  // namespace mtp

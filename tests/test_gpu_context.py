@@ -4,7 +4,7 @@ oracle's FP64 rows: each element within the final rounding plus the FP32
 summation bound (a plain one-ulp bound fails where the sum nearly cancels),
 almost all bit-equal (tests/harness.py, `check_eh_proj_rows`).  Covers the
 single-row kernel, the batched split-K sweep (2..16 rows) and the tiled MFMA
-GEMM in its tile shapes (128 x 128 with 64-column steps for 17..255 rows,
+GEMM in its tile shapes (128 x 128 with 64-column steps for 17..128 rows,
 256 x 256 or 256 x 192 beyond; split over K for few tiles, with ragged row,
 column and K tiles)."""
 import numpy as np
@@ -49,7 +49,7 @@ def _run(H, V, T, seed, bad_row=None, sample=None):
     (256, 3000, 37, 82), (256, 3000, 64, 83),
     (256, 3000, 65, 84), (256, 3000, 200, 85), (1040, 2000, 65, 86), (1040, 2000, 130, 87),
     (512, 4000, 300, 88), (1040, 2000, 600, 94), (256, 3000, 255, 95), (256, 3000, 256, 96),
-    (1040, 2000, 40, 98),
+    (1040, 2000, 40, 98), (256, 3000, 128, 97), (256, 3000, 129, 99),
 ])
 def test_context_rows(H, V, T, seed):
     _run(H, V, T, seed)
