@@ -26,9 +26,12 @@
 // norms are computed.  Grids are a multiple of the CU count so every CU gets
 // the same number of workgroups.
 //
-// Sums are FP32 in a fixed order (per lane over its chunks, then a fixed xor
-// butterfly), so results do not depend on grid size or timing; the argmax
-// order (value, then lower index) is associative, so neither does the draft.
+// Sums are FP32 in a fixed order (per lane over its chunks, then DPP moves
+// within each 16-lane row and the four row sums in row order), so results do
+// not depend on grid size or timing; the argmax order (value, then lower
+// index) is associative, so neither does the draft.
+#include <type_traits>
+
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -60,6 +63,27 @@ __device__ __forceinline__ float dot4_fp8(uint32_t q, uint32_t a01, uint32_t a23
     acc = fmaf(d23.x, bf16_lo(a23), acc);
     acc = fmaf(d23.y, bf16_hi(a23), acc);
     return acc;
+}
+
+// Sum of a value over the 64 lanes of a wave, the same in every lane: DPP
+// moves within each 16-lane row (pairs, quads, half-row mirror, row mirror),
+// then the four row sums read into scalars and added in row order.  No LDS
+// round trips (an xor butterfly of lane shuffles costs six).
+__device__ __forceinline__ float row_sum64(float v)
+{
+    auto dpp = [](float x, auto ctrl) {
+        return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), decltype(ctrl)::value,
+                                                       0xF, 0xF, true));
+    };
+    v += dpp(v, std::integral_constant<int, 0xB1>{});   // quad_perm [1, 0, 3, 2]
+    v += dpp(v, std::integral_constant<int, 0x4E>{});   // quad_perm [2, 3, 0, 1]
+    v += dpp(v, std::integral_constant<int, 0x141>{});  // row_half_mirror
+    v += dpp(v, std::integral_constant<int, 0x140>{});  // row_mirror
+    const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
+    const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
+    const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
+    const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
+    return ((r0 + r1) + r2) + r3;
 }
 
 // Weight stream loads.  With NT the load carries the non-temporal hint: the
@@ -211,7 +235,7 @@ __global__ __launch_bounds__(BS) void row_gemv_kernel(RowGemvArgs a)
 #pragma unroll
         for (int k = 0; k < RPI; ++k) {
             const int r = r0 + k * r_inner;
-            const float sum = wave_sum(acc[k]);
+            const float sum = row_sum64(acc[k]);
             acc[k] = 0.f;
             if (r < r_end) {
                 if (EPI == EPI_STORE) {
