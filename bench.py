@@ -287,7 +287,7 @@ def main():
             # the first Vs rows of each [V][H] table (the head reads no embedding)
             sw = mtp.mtp_weights(t["embed"][:Vs], t["enorm_w"], t["hnorm_w"], t["head_norm_w"],
                                  t["eh_proj"], t["lm_head"][:Vs], float(wts["rms_eps"]))
-            slg = logits[:, :Vs]
+            slg = torch.empty((B, Vs), dtype=torch.bfloat16, device=dev)
             sws = mtp.new_workspace(H, Vs, B)
             ent = {"rows": Vs}
             for name, fp8 in (("bf16", False), ("fp8", True)):
