@@ -28,6 +28,8 @@ import numpy as np
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "oracle.c")
 _LIB = os.path.join(_HERE, "liboracle.so")
+# A test may point this at another build of oracle.c (a sanitizer build).
+_LIB_OVERRIDE = os.environ.get("MTP_ORACLE_LIB")
 
 GCC_CMD = ["gcc", "-O2", "-ffp-contract=off", "-fno-fast-math", "-std=c11", "-Wall",
            "-shared", "-fPIC", "-pthread", _SRC, "-o", _LIB, "-lm"]
@@ -45,9 +47,12 @@ _lib = None
 def lib():
     global _lib
     if _lib is None:
-        if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
-            build()
-        L = ctypes.CDLL(_LIB)
+        if _LIB_OVERRIDE:
+            L = ctypes.CDLL(_LIB_OVERRIDE)
+        else:
+            if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+                build()
+            L = ctypes.CDLL(_LIB)
         P = ctypes.c_void_p
         i64 = ctypes.c_int64
         L.orc_bf16_to_double.argtypes = [ctypes.c_uint16]
@@ -60,6 +65,8 @@ def lib():
         L.orc_e4m3_encode.restype = ctypes.c_uint8
         L.orc_rmsnorm.argtypes = [P, P, i64, ctypes.c_float, P]
         L.orc_rmsnorm.restype = None
+        L.orc_rmsnorm_unrounded.argtypes = [P, P, i64, ctypes.c_float, P]
+        L.orc_rmsnorm_unrounded.restype = None
         L.orc_front.argtypes = [P, i64, i64, ctypes.c_uint32, P, P, P, ctypes.c_float, P]
         L.orc_front.restype = ctypes.c_int
         L.orc_gemv_bf16.argtypes = [P, i64, i64, P, P, ctypes.c_int]
@@ -81,8 +88,36 @@ def _p(a: np.ndarray):
     return ctypes.c_void_p(a.ctypes.data)
 
 
+def host_cores() -> dict:
+    """What this process may run on: os.cpu_count(), the CPU affinity mask and
+    the cgroup CPU quota (in cores, None when unlimited)."""
+    info = {"os_cpu_count": os.cpu_count() or 1,
+            "affinity": len(os.sched_getaffinity(0)), "cgroup_quota_cores": None}
+    for path, split in (("/sys/fs/cgroup/cpu.max", None),
+                        ("/sys/fs/cgroup/cpu/cpu.cfs_quota_us", "/sys/fs/cgroup/cpu/cpu.cfs_period_us")):
+        try:
+            if split is None:
+                quota, period = open(path).read().split()
+            else:
+                quota, period = open(path).read().strip(), open(split).read().strip()
+            if quota not in ("max", "-1"):
+                info["cgroup_quota_cores"] = -(-int(quota) // int(period))
+            break
+        except (OSError, ValueError):
+            continue
+    return info
+
+
+# A GPU box grants one process about 16 host cores whatever the machine has.
+THREAD_CAP = 16
+
+
 def default_threads() -> int:
-    return max(1, min(16, os.cpu_count() or 1))
+    """Threads for the row-parallel loops: the cores this process may use
+    (affinity, cgroup quota), at most THREAD_CAP."""
+    h = host_cores()
+    n = min(h["os_cpu_count"], h["affinity"], h["cgroup_quota_cores"] or h["affinity"])
+    return max(1, min(THREAD_CAP, n))
 
 
 # --------------------------------------------------------------------------
@@ -121,6 +156,27 @@ def rmsnorm(x: np.ndarray, w: np.ndarray, eps: float) -> np.ndarray:
     out = np.empty_like(x)
     lib().orc_rmsnorm(_p(x), _p(w), x.size, ctypes.c_float(eps), _p(out))
     return out
+
+
+def rmsnorm_unrounded(x: np.ndarray, w: np.ndarray, eps: float) -> np.ndarray:
+    """The norm's outputs in FP64 before their BF16 rounding (rmsnorm rounds
+    exactly these values)."""
+    x = np.ascontiguousarray(x, dtype=np.uint16)
+    w = np.ascontiguousarray(w, dtype=np.uint16)
+    out = np.empty(x.size, dtype=np.float64)
+    lib().orc_rmsnorm_unrounded(_p(x), _p(w), x.size, ctypes.c_float(eps), _p(out))
+    return out
+
+
+def front_unrounded(embed, token: int, hidden, enorm_w, hnorm_w, eps: float):
+    """[enorm(embed[token]) | hnorm(hidden)] in FP64 before the BF16 rounding
+    of the concat; None when token >= V."""
+    V, H = embed.shape
+    if int(token) >= V:
+        return None
+    e = np.ascontiguousarray(embed[int(token)])
+    return np.concatenate([rmsnorm_unrounded(e, enorm_w, eps),
+                           rmsnorm_unrounded(np.ascontiguousarray(hidden), hnorm_w, eps)])
 
 
 def front(embed, token: int, hidden, enorm_w, hnorm_w, eps: float):
@@ -186,6 +242,7 @@ def draft(w: dict, token: int, hidden: np.ndarray, fp8: tuple | None = None,
     concat = front(w["embed"], token, hidden, w["enorm_w"], w["hnorm_w"], eps)
     if concat is None:
         return None
+    concat_un = front_unrounded(w["embed"], token, hidden, w["enorm_w"], w["hnorm_w"], eps)
     x_un = gemv_bf16(w["eh_proj"], concat, nthreads)
     x = bf16_from_f64(x_un)
     xn = rmsnorm(x, w["head_norm_w"], eps)
@@ -194,7 +251,8 @@ def draft(w: dict, token: int, hidden: np.ndarray, fp8: tuple | None = None,
     else:
         o = gemv_fp8(fp8[0], fp8[1], xn, nthreads)
     logits = bf16_from_f64(o)
-    return {"concat": concat, "x_unrounded": x_un, "x": x, "xn": xn, "o": o,
+    return {"concat": concat, "concat_unrounded": concat_un, "x_unrounded": x_un, "x": x,
+            "xn": xn, "o": o,
             "logits": logits, "draft": argmax_bf16(logits)}
 
 
@@ -202,23 +260,27 @@ def context_rows(w: dict, tokens: np.ndarray, hiddens: np.ndarray,
                  nthreads: int | None = None) -> dict:
     """Context rows (glm5next_mtp_head.rs, `rows_impl`): row r pairs the
     embedding of tokens[r + 1] with hiddens[r] and runs enorm, hnorm, concat and
-    eh_proj.  Returns ``x`` as BF16 bits [T][H], ``x_unrounded`` (FP64) and the
-    BF16 ``concat`` rows [T][2H]; all zero in a row whose tokens[r + 1] is out
-    of range (the library leaves such a row unspecified)."""
+    eh_proj.  Returns ``x`` as BF16 bits [T][H], ``x_unrounded`` (FP64), the
+    BF16 ``concat`` rows [T][2H] and ``concat_unrounded`` (FP64, before that
+    rounding); all zero in a row whose tokens[r + 1] is out of range (the
+    library leaves such a row unspecified)."""
     T = hiddens.shape[0]
     assert tokens.size == T + 1
     H = w["embed"].shape[1]
     x = np.zeros((T, H), dtype=np.uint16)
     x_un = np.zeros((T, H), dtype=np.float64)
     concat = np.zeros((T, 2 * H), dtype=np.uint16)
+    concat_un = np.zeros((T, 2 * H), dtype=np.float64)
     for r in range(T):
         c = front(w["embed"], int(tokens[r + 1]), hiddens[r], w["enorm_w"], w["hnorm_w"],
                   float(w["rms_eps"]))
         if c is not None:
             concat[r] = c
+            concat_un[r] = front_unrounded(w["embed"], int(tokens[r + 1]), hiddens[r],
+                                           w["enorm_w"], w["hnorm_w"], float(w["rms_eps"]))
             x_un[r] = gemv_bf16(w["eh_proj"], c, nthreads)
             x[r] = bf16_from_f64(x_un[r])
-    return {"x": x, "x_unrounded": x_un, "concat": concat}
+    return {"x": x, "x_unrounded": x_un, "concat": concat, "concat_unrounded": concat_un}
 
 
 def draft_chain(w: dict, token: int, hidden: np.ndarray, steps: int, fp8: tuple | None = None,

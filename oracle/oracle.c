@@ -124,16 +124,31 @@ uint8_t orc_e4m3_encode(float y)
 
 /* rms_norm_vanilla ([LAYER] invariants; launched by `norm` in [MTP]):
  * out_j = BF16(x_j * w_j / sqrt(sum_i x_i^2 / n + eps)). */
-void orc_rmsnorm(const uint16_t *x, const uint16_t *w, int64_t n, float eps, uint16_t *out)
+static double rms_of(const uint16_t *x, int64_t n, float eps)
 {
     double ss = 0.0;
     for (int64_t j = 0; j < n; ++j) {
         double v = orc_bf16_to_double(x[j]);
         ss += v * v;
     }
-    double r = sqrt(ss / (double)n + (double)eps);
+    return sqrt(ss / (double)n + (double)eps);
+}
+
+void orc_rmsnorm(const uint16_t *x, const uint16_t *w, int64_t n, float eps, uint16_t *out)
+{
+    double r = rms_of(x, n, eps);
     for (int64_t j = 0; j < n; ++j)
         out[j] = orc_bf16_from_double(orc_bf16_to_double(x[j]) * orc_bf16_to_double(w[j]) / r);
+}
+
+/* The same norm with each output left in FP64, before the BF16 rounding that
+ * orc_rmsnorm applies: the value every stored element is rounded from. */
+void orc_rmsnorm_unrounded(const uint16_t *x, const uint16_t *w, int64_t n, float eps,
+                           double *out)
+{
+    double r = rms_of(x, n, eps);
+    for (int64_t j = 0; j < n; ++j)
+        out[j] = orc_bf16_to_double(x[j]) * orc_bf16_to_double(w[j]) / r;
 }
 
 /* Gather + enorm + hnorm + concat ([MTP] module doc and `forward_one`):

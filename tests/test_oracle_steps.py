@@ -96,6 +96,40 @@ def test_norm_exact_rationals(orc, H):
         assert np.array_equal(orc.rmsnorm(x, w, EPS), exact_norm(x, w)), trial
 
 
+@pytest.mark.parametrize("H", [1, 2, 5, 16])
+def test_norm_unrounded_exact_rationals(orc, H):
+    """The norm's FP64 values before rounding: within 1e-14 (relative) of the
+    exact x_j w_j / sqrt(mean(x^2) + eps), and rounding them gives the
+    rounded norm's outputs bit for bit."""
+    g = np.random.default_rng(300 + H)
+    for trial in range(20):
+        x = rand_bf16(g, H, 10.0 ** g.uniform(-3, 2))
+        w = rand_bf16(g, H, 0.3, 1.0)
+        u = orc.rmsnorm_unrounded(x, w, EPS)
+        xs = [exact.bf16_exact(v) for v in x]
+        ws = [exact.bf16_exact(v) for v in w]
+        r = exact.dec_sqrt(sum(v * v for v in xs) / len(xs) + EPS_EXACT)
+        for j in range(H):
+            p = xs[j] * ws[j]
+            want = Decimal(p.numerator) / Decimal(p.denominator) / r
+            assert abs(Decimal(float(u[j])) - want) <= abs(want) * Decimal("1e-14"), (trial, j)
+        assert np.array_equal(orc.bf16_from_f64(u), orc.rmsnorm(x, w, EPS)), trial
+
+
+def test_norm_unrounded_closed_forms(orc):
+    """w = 1, x = e_k at H = 256: 16 exactly at k, zeros elsewhere; w = 1,
+    x = c * ones: c / sqrt(c^2 + eps) in every lane."""
+    H, k = 256, 37
+    x = np.zeros(H, np.uint16)
+    x[k] = ONE
+    u = orc.rmsnorm_unrounded(x, np.full(H, ONE, np.uint16), EPS)
+    assert abs(u[k] - 16.0 / np.sqrt(1.0 + 256.0 * float(np.float32(EPS)))) < 1e-13
+    assert np.all(np.delete(u, k) == 0.0)
+    c = float(exact.bf16_exact(int(bf([3.0])[0])))
+    u = orc.rmsnorm_unrounded(bf([3.0] * 64), np.full(64, ONE, np.uint16), EPS)
+    assert np.allclose(u, c / np.sqrt(c * c + float(np.float32(EPS))), rtol=1e-15, atol=0)
+
+
 def test_norm_eps_matters(orc):
     """A tiny row, where eps dominates: sqrt(mean(x^2) + eps), eps as f32."""
     H = 8
@@ -135,7 +169,11 @@ def test_front_gather_and_bounds(orc):
         c = orc.front(w["embed"], tok, hid, w["enorm_w"], w["hnorm_w"], EPS)
         assert np.array_equal(c[:H], exact_norm(w["embed"][tok], w["enorm_w"]))
         assert np.array_equal(c[H:], exact_norm(hid, w["hnorm_w"]))
+        # the unrounded concat: same order, and it rounds to the concat
+        u = orc.front_unrounded(w["embed"], tok, hid, w["enorm_w"], w["hnorm_w"], EPS)
+        assert np.array_equal(orc.bf16_from_f64(u), c)
     assert orc.front(w["embed"], V, hid, w["enorm_w"], w["hnorm_w"], EPS) is None
+    assert orc.front_unrounded(w["embed"], V, hid, w["enorm_w"], w["hnorm_w"], EPS) is None
     assert orc.front(w["embed"], 2 ** 32 - 1, hid, w["enorm_w"], w["hnorm_w"], EPS) is None
 
 
