@@ -39,7 +39,8 @@ def _run(H, V, T, seed, bad_row=None, sample=None):
     # the oracle on the chosen rows only: row r needs tokens[r + 1] and hiddens[r]
     sub_tok = np.concatenate([[0], tokens[np.array(rows) + 1]]).astype(tokens.dtype)
     ref = oracle.context_rows(wts, sub_tok, np.ascontiguousarray(hiddens[rows]))
-    st = harness.check_eh_proj_rows(xg[rows], ref["x_unrounded"], ref["concat"], wts["eh_proj"])
+    st = harness.check_eh_proj_rows(xg[rows], ref["x_unrounded"], ref["concat"],
+                                    ref["concat_unrounded"], wts["eh_proj"])
     print(f"[context] {st}", flush=True)
     return xg
 

@@ -237,7 +237,7 @@ def test_front_and_head_entry_points():
         r = oracle.draft(wts, int(tokens[b]), hidden[b])
         xs.append(r["x"])
         harness.check_eh_proj_rows(xg[b:b + 1], r["x_unrounded"][None], r["concat"][None],
-                                   wts["eh_proj"])
+                                   r["concat_unrounded"][None], wts["eh_proj"])
     xo = harness.to_dev_bf16(np.stack(xs))
     for fp8 in (False, True):
         dr = torch.empty(B, dtype=torch.int32, device="cuda")
