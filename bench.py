@@ -102,14 +102,115 @@ def sweep_bytes(H: int, V: int, B: int, fp8: bool) -> int:
     return 2 * H * H * 2 + head_bytes(H, V, B, fp8) + B * 2 * H * 2 + 2 * H * 2
 
 
-def cpu_model() -> str:
+def cpu_info() -> dict:
+    """The host CPU as /proc/cpuinfo names it, and how many processors it lists."""
+    info = {"model_name": "unknown", "vendor_id": None, "cpu_family": None, "model": None,
+            "processors_listed": 0}
+    keys = {"model name": "model_name", "vendor_id": "vendor_id", "cpu family": "cpu_family",
+            "model": "model"}
     try:
         for line in open("/proc/cpuinfo"):
-            if line.startswith("model name"):
-                return line.split(":", 1)[1].strip()
+            if ":" not in line:
+                continue
+            k, v = (t.strip() for t in line.split(":", 1))
+            if k == "processor":
+                info["processors_listed"] += 1
+            elif k in keys and info["processors_listed"] <= 1:
+                info[keys[k]] = v
     except OSError:
         pass
-    return "unknown"
+    return info
+
+
+def _time_calls(fn, seconds: float):
+    """Run fn until `seconds` have passed (at least once): (calls, elapsed s)."""
+    n, t0 = 0, time.perf_counter()
+    while True:
+        fn()
+        n += 1
+        el = time.perf_counter() - t0
+        if el >= seconds:
+            return n, el
+
+
+def cpu_baseline_leg(args, cfg, wts, tokens, hidden) -> dict:
+    """The FP64 oracle timed on the host: the bench configuration's BF16 sweep
+    (the reported value), then every configuration and head path for a bounded
+    time each, the quantiser, and one-thread figures from row samples."""
+    import numpy as np
+
+    import oracle
+    import synth
+
+    nthreads = oracle.default_threads()
+    H, V, B = cfg.hidden, cfg.vocab, cfg.batch
+
+    def sweeps(w, tk, hd, fp8=None, nt=nthreads):
+        for b in range(tk.size):
+            oracle.draft(w, int(tk[b]), hd[b], fp8=fp8, nthreads=nt)
+
+    n, el = _time_calls(lambda: sweeps(wts, tokens, hidden), args.cpu_seconds * 0.5)
+    cpu = {"value": round(n / el, 4), "unit": "draft sweeps/s" if B == 1 else "calls/s",
+           "cores": nthreads, "kind": "oracle",
+           "sample": f"{n} full {cfg.name} BF16 draft sweep call(s) (B={B}) through the FP64 "
+                     f"oracle in {el:.1f}s on {nthreads} threads splitting vocab rows"}
+    hc = oracle.host_cores()
+    detail = {"cpu": cpu_info(), "host_cores": hc, "threads": nthreads,
+              "thread_rule": f"min(os.cpu_count(), affinity, cgroup quota, {oracle.THREAD_CAP}): "
+                             f"a GPU box grants one process about {oracle.THREAD_CAP} host cores"}
+    # the FP8 copy of the bench weights (timed: the quantiser on the host)
+    tq = time.perf_counter()
+    ref8 = oracle.quantize_fp8(wts["lm_head"], nthreads=nthreads)
+    detail["quantiser_s"] = round(time.perf_counter() - tq, 3)
+
+    # every configuration and path, each for about a second (one call at least);
+    # batched and near-tie share the large shape, so they run on the bench's
+    # weights with their own tokens and hidden rows (values do not change the
+    # oracle's cost)
+    per_s = max(0.5, args.cpu_seconds / 12)
+    per = {}
+    own = {(H, V): (wts, ref8)}
+    for name, paths in (("tiny", ("bf16", "fp8")), ("mid", ("bf16",)),
+                        ("large", ("bf16", "fp8")), ("batched", ("fp8",)),
+                        ("neartie", ("bf16", "fp8"))):
+        c = synth.CONFIGS[name]
+        if (c.hidden, c.vocab) not in own:
+            w2 = synth.make_weights(c)
+            own[(c.hidden, c.vocab)] = (w2, oracle.quantize_fp8(w2["lm_head"], nthreads=nthreads)
+                                        if "fp8" in paths else None)
+        w2, r8 = own[(c.hidden, c.vocab)]
+        tk, hd = synth.make_inputs(c)
+        ent = {"hidden": c.hidden, "vocab": c.vocab, "batch": c.batch}
+        for path in paths:
+            n2, el2 = _time_calls(lambda: sweeps(w2, tk, hd, r8 if path == "fp8" else None), per_s)
+            ent[path] = {"calls_per_s": round(n2 / el2, 4),
+                         "sequences_per_s": round(n2 * c.batch / el2, 4),
+                         "ms_per_call": round(el2 / n2 * 1e3, 2), "calls": n2}
+        per[name] = ent
+        if name == "mid":
+            del own[(c.hidden, c.vocab)]  # 2.5 GB of weights no longer needed
+    detail["per_config"] = per
+
+    # one thread: eh_proj whole, row samples of lm_head and of the quantiser,
+    # scaled to the whole matrix (every row costs the same)
+    rows = min(V, 16384)
+    xs = synth.to_bf16(np.ones(H, np.float32))
+    cs = synth.to_bf16(np.ones(2 * H, np.float32))
+    t1 = time.perf_counter()
+    oracle.gemv_bf16(wts["eh_proj"], cs, nthreads=1)
+    t_front = time.perf_counter() - t1
+    t1 = time.perf_counter()
+    oracle.gemv_bf16(wts["lm_head"][:rows], xs, nthreads=1)
+    t_head = (time.perf_counter() - t1) * V / rows
+    detail["bf16_sweeps_per_s_1thread"] = round(1.0 / (t_front + t_head), 4)
+    t1 = time.perf_counter()
+    oracle.quantize_fp8(wts["lm_head"][:rows // 4], nthreads=1)
+    detail["quantiser_s_1thread"] = round((time.perf_counter() - t1) * V / (rows // 4), 3)
+    detail["one_thread_sample"] = (f"eh_proj GEMV whole, lm_head GEMV over {rows} rows and "
+                                   f"the quantiser over {rows // 4} rows, scaled to {V} rows")
+    cpu["detail"] = detail
+    print(f"[bench] cpu baseline: {cpu}", file=sys.stderr, flush=True)
+    return cpu
 
 
 def main():
@@ -398,28 +499,48 @@ def main():
     if not args.no_agreement:
         # How often the FP8 drafting copy proposes the same token as the BF16
         # head (the page's reason for the copy: it may change acceptance, never
-        # an emitted token).  Random-init weights: a synthetic proxy only.
-        acfg = synth.custom(H, V, 64, 2001)
-        atok, ahid = synth.make_inputs(acfg)
-        Ba = acfg.batch
-        atk = torch.from_numpy(atok.astype(np.uint32).view(np.int32)).to(dev)
-        ahd = harness.to_dev_bf16(ahid)
-        adr16 = torch.empty(Ba, dtype=torch.int32, device=dev)
-        adr8 = torch.empty(Ba, dtype=torch.int32, device=dev)
-        alg16 = torch.empty((Ba, V), dtype=torch.bfloat16, device=dev)
-        aws = mtp.new_workspace(H, V, Ba)
-        mtp.mtp_draft_bf16(dw.w, Ba, atk, ahd, adr16, alg16, aws, stream)
-        mtp.mtp_draft_fp8w(dw.w, q, s, Ba, atk, ahd, adr8, None, aws, stream)
-        torch.cuda.synchronize()
-        d16 = adr16.cpu().numpy()
-        d8 = adr8.cpu().numpy()
-        lg16 = alg16.float()
-        top2 = torch.topk(lg16, 2, dim=1).values.cpu().numpy()
-        gaps = top2[:, 0] - top2[:, 1]
-        agree = int((d16 == d8).sum())
-        agreement = {"sequences": Ba, "agree": agree, "rate": round(agree / Ba, 4),
-                     "median_bf16_top2_gap": round(float(np.median(gaps)), 4),
-                     "data": "synthetic random-init weights (a proxy, not an acceptance rate)"}
+        # an emitted token).  Random-init weights: a synthetic proxy only.  The
+        # oracle's own rate on the same sequences comes from the agreement
+        # tests, which need minutes of FP64 work.
+        def agree_on(w, qq, ss, Hh, Vv, atok, ahid):
+            n = atok.size
+            d16 = np.empty(n, np.int64)
+            d8 = np.empty(n, np.int64)
+            gaps = np.empty(n)
+            for b0 in range(0, n, 64):
+                bb = min(64, n - b0)
+                atk = torch.from_numpy(atok[b0:b0 + bb].astype(np.uint32).view(np.int32)).to(dev)
+                ahd = harness.to_dev_bf16(np.ascontiguousarray(ahid[b0:b0 + bb]))
+                a16 = torch.empty(bb, dtype=torch.int32, device=dev)
+                a8 = torch.empty(bb, dtype=torch.int32, device=dev)
+                alg = torch.empty((bb, Vv), dtype=torch.bfloat16, device=dev)
+                aws = mtp.new_workspace(Hh, Vv, bb)
+                mtp.mtp_draft_bf16(w, bb, atk, ahd, a16, alg, aws, stream)
+                mtp.mtp_draft_fp8w(w, qq, ss, bb, atk, ahd, a8, None, aws, stream)
+                torch.cuda.synchronize()
+                d16[b0:b0 + bb] = a16.cpu().numpy()
+                d8[b0:b0 + bb] = a8.cpu().numpy()
+                top2 = torch.topk(alg.float(), 2, dim=1).values.cpu().numpy()
+                gaps[b0:b0 + bb] = top2[:, 0] - top2[:, 1]
+            agree = int((d16 == d8).sum())
+            return {"sequences": n, "agree": agree, "rate": round(agree / n, 4),
+                    "median_bf16_top2_gap": round(float(np.median(gaps)), 4)}
+
+        agreement = {"data": "synthetic random-init weights (a proxy, not an acceptance rate)"}
+        if args.config == "large":
+            tw = synth.make_weights(synth.CONFIGS["tiny"])
+            tdw = harness.upload(tw)
+            tq, ts = harness.quantize_dev(tdw)
+            ttok, thid = synth.make_inputs(synth.custom(256, 4096, 256, 3001))
+            agreement["tiny"] = agree_on(tdw.w, tq, ts, 256, 4096, ttok, thid)
+            atok, ahid = synth.make_inputs(synth.custom(H, V, 64, 2001))
+            agreement["large"] = agree_on(dw.w, q, s, H, V, atok, ahid)
+            btok, bhid = synth.make_inputs(synth.CONFIGS["batched"])
+            agreement["batched_inputs_on_large_weights"] = agree_on(dw.w, q, s, H, V, btok, bhid)
+            del tdw, tq, ts
+        else:
+            atok, ahid = synth.make_inputs(synth.custom(H, V, 64, 2001))
+            agreement[cfg.name] = agree_on(dw.w, q, s, H, V, atok, ahid)
         print(f"[bench] agreement: {agreement}", file=sys.stderr, flush=True)
 
     if args.calib_copy:
@@ -462,68 +583,20 @@ def main():
         "peak": HBM_PEAK_GBPS,
         "unit": "GB/s",
         "frac": round(r["lm_head_GBps"] / HBM_PEAK_GBPS, 4),
-        "traffic": committed_traffic("lm_head_bf16_large_traffic.md"),
+        "traffic": committed_traffic(f"lm_head_bf16_{cfg.name}_traffic.md"),
         "kernel": "row_gemv_kernel<BF16, head-norm prologue, argmax-partials epilogue>; the "
                   "timed mtp_head_bf16 call also runs the one-workgroup-per-sequence "
                   "argmax_final_kernel after it",
-        "traffic_source": "profiles/lm_head_bf16_large_traffic.md (null when the kernel "
-                          "sources changed since the counters were taken)",
+        "traffic_source": f"profiles/lm_head_bf16_{cfg.name}_traffic.md (null when there is "
+                          "none for this configuration or the kernel sources changed since the "
+                          "counters were taken)",
         "algorithmic_bytes_per_launch": hb,
         "avg_launch_us": round(r["head_us"], 2),
     }
 
     cpu = None
     if not args.no_cpu_baseline:
-        import oracle
-        nthreads = oracle.default_threads()
-        t_end = time.perf_counter() + args.cpu_seconds
-        n = 0
-        tc = time.perf_counter()
-        while True:
-            for b in range(B):
-                oracle.draft(wts, int(tokens[b]), hidden[b], nthreads=nthreads)
-            n += 1
-            if time.perf_counter() >= t_end:
-                break
-        el = time.perf_counter() - tc
-        cpu = {"value": round(n / el, 4), "unit": "draft sweeps/s", "cores": nthreads,
-               "kind": "oracle",
-               "sample": f"{n} full {cfg.name} BF16 draft sweep(s) (B={B}) through the FP64 "
-                         f"oracle, {el:.1f}s, {nthreads} threads splitting vocab rows"}
-        # the same oracle on one thread, the FP8 head path, and the quantiser;
-        # the one-thread figures time row samples of the same matrices and
-        # scale them to the whole sweep (every row costs the same)
-        detail = {"cpu_model": cpu_model()}
-        tq = time.perf_counter()
-        q_or, s_or = oracle.quantize_fp8(wts["lm_head"], nthreads=nthreads)
-        detail["quantiser_s"] = round(time.perf_counter() - tq, 3)
-        detail["quantiser_threads"] = nthreads
-        n8, t_end = 0, time.perf_counter() + 3.0
-        tc = time.perf_counter()
-        while True:
-            for b in range(B):
-                oracle.draft(wts, int(tokens[b]), hidden[b], fp8=(q_or, s_or), nthreads=nthreads)
-            n8 += 1
-            if time.perf_counter() >= t_end:
-                break
-        detail["fp8_sweeps_per_s"] = round(n8 / (time.perf_counter() - tc), 4)
-        rows = min(V, 16384)
-        xs = synth.to_bf16(np.ones(H, np.float32))
-        cs = synth.to_bf16(np.ones(2 * H, np.float32))
-        t1 = time.perf_counter()
-        oracle.gemv_bf16(wts["eh_proj"], cs, nthreads=1)
-        t_front = time.perf_counter() - t1
-        t1 = time.perf_counter()
-        oracle.gemv_bf16(wts["lm_head"][:rows], xs, nthreads=1)
-        t_head = (time.perf_counter() - t1) * V / rows
-        detail["bf16_sweeps_per_s_1thread"] = round(1.0 / (t_front + t_head), 4)
-        t1 = time.perf_counter()
-        oracle.quantize_fp8(wts["lm_head"][:rows // 4], nthreads=1)
-        detail["quantiser_s_1thread"] = round((time.perf_counter() - t1) * V / (rows // 4), 3)
-        detail["one_thread_sample"] = (f"eh_proj GEMV whole, lm_head GEMV over {rows} rows and "
-                                       f"the quantiser over {rows // 4} rows, scaled to {V} rows")
-        cpu["detail"] = detail
-
+        cpu = cpu_baseline_leg(args, cfg, wts, tokens, hidden)
     line = {
         "metric": METRIC,
         "value": round(r["sweeps_per_s"], 2),
