@@ -25,7 +25,8 @@
  *  - Device pointers are HIP device addresses; the caller owns every buffer and
  *    the stream and keeps them alive until the enqueued work completes.  The
  *    library allocates, frees and retains nothing and has no mutable global
- *    state; calls on different streams need distinct workspaces.
+ *    state, except the static scratch of mtp_draft_static; calls on different
+ *    streams need distinct workspaces.
  *  - `stream` is a hipStream_t passed as void* (NULL = the null stream).
  *  - Layouts are row-major and densely packed.  Every device pointer must be
  *    16-byte aligned.
@@ -58,7 +59,9 @@ enum {
     MTP_ERR_ALIGN = 3,     /* a device pointer is not 16-byte aligned           */
     MTP_ERR_WORKSPACE = 4, /* workspace NULL or smaller than mtp_workspace_bytes */
     MTP_ERR_NONFINITE = 5, /* quantiser: a weight is NaN or Inf                  */
-    MTP_ERR_HIP = 6        /* a HIP runtime call or kernel launch failed        */
+    MTP_ERR_HIP = 6,       /* a HIP runtime call or kernel launch failed        */
+    MTP_ERR_SCRATCH = 7    /* mtp_draft_static: the shape needs more than
+                              MTP_STATIC_SCRATCH_BYTES of scratch              */
 };
 
 #define MTP_DRAFT_INVALID 0xFFFFFFFFu /* draft[b] when tokens[b] >= vocab */
@@ -67,6 +70,7 @@ enum {
 #define MTP_MAX_BATCH 64
 #define MTP_MAX_CONTEXT_ROWS 65536
 #define MTP_MAX_CHAIN_STEPS 64
+#define MTP_STATIC_SCRATCH_BYTES (16u << 20) /* scratch of mtp_draft_static, per GPU */
 
 /* The drafter's weights, all BF16 device arrays (glm5next_mtp_head.rs: the
  * head owns `embed_tokens`, the target's `lm_head`, and the MTP module's
@@ -134,6 +138,28 @@ int mtp_draft_bf16(const mtp_weights *w, int32_t batch, const uint32_t *tokens,
 int mtp_draft_fp8w(const mtp_weights *w, const uint8_t *q, const float *scale, int32_t batch,
                    const uint32_t *tokens, const void *hidden, uint32_t *draft, void *logits,
                    void *workspace, size_t ws_bytes, void *stream);
+
+/* Allocation-free draft call, for callers that cannot allocate device memory
+ * or pass a workspace (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation).  The same sweep as mtp_draft_bf16 (q and
+ * scale both NULL: the BF16 lm_head) or mtp_draft_fp8w (q and scale both
+ * non-NULL: the FP8 copy), with the same arguments, results and errors, minus
+ * the workspace: its scratch is a static device array of
+ * MTP_STATIC_SCRATCH_BYTES inside the library, one per GPU, held until the
+ * process ends.  The call allocates nothing.
+ *  - A shape whose workspace (mtp_workspace_bytes) exceeds
+ *    MTP_STATIC_SCRATCH_BYTES returns MTP_ERR_SCRATCH before anything is
+ *    enqueued; at H = 6144 every batch up to 32 fits.
+ *  - Every call on one GPU shares that GPU's scratch, which keeps the last
+ *    call's contents (no call needs it cleared): calls that can overlap on one
+ *    GPU (different streams, or different host threads) race and must be
+ *    serialised by the caller.
+ *  - The first call on a GPU resolves the scratch's device address (a runtime
+ *    query, no allocation); make that call outside graph capture.
+ * Asynchronous on `stream`. */
+int mtp_draft_static(const mtp_weights *w, const uint8_t *q, const float *scale, int32_t batch,
+                     const uint32_t *tokens, const void *hidden, uint32_t *draft, void *logits,
+                     void *stream);
 
 /* The front half alone (glm5next_mtp_head.rs, `forward_one` up to the block):
  * gather, enorm, hnorm, concat and eh_proj, writing the block input

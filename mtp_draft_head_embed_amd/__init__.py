@@ -17,15 +17,17 @@ import torch
 
 __all__ = [
     "MTP_OK", "MTP_ERR_NULL", "MTP_ERR_SHAPE", "MTP_ERR_ALIGN", "MTP_ERR_WORKSPACE",
-    "MTP_ERR_NONFINITE", "MTP_ERR_HIP", "MTP_DRAFT_INVALID", "MtpError", "mtp_weights",
+    "MTP_ERR_NONFINITE", "MTP_ERR_HIP", "MTP_ERR_SCRATCH", "MTP_STATIC_SCRATCH_BYTES",
+    "MTP_DRAFT_INVALID", "MtpError", "mtp_weights",
     "lib", "lib_path", "mtp_workspace_bytes", "mtp_validate_draft_args",
     "mtp_quantize_head_fp8", "mtp_draft_bf16", "mtp_draft_fp8w", "mtp_front", "mtp_head_bf16",
     "mtp_head_fp8w", "mtp_status_str", "new_workspace", "mtp_context_workspace_bytes",
-    "mtp_context_rows", "mtp_probe_stream_read",
+    "mtp_context_rows", "mtp_probe_stream_read", "mtp_draft_static",
 ]
 
 MTP_OK, MTP_ERR_NULL, MTP_ERR_SHAPE, MTP_ERR_ALIGN = 0, 1, 2, 3
-MTP_ERR_WORKSPACE, MTP_ERR_NONFINITE, MTP_ERR_HIP = 4, 5, 6
+MTP_ERR_WORKSPACE, MTP_ERR_NONFINITE, MTP_ERR_HIP, MTP_ERR_SCRATCH = 4, 5, 6, 7
+MTP_STATIC_SCRATCH_BYTES = 16 << 20
 MTP_DRAFT_INVALID = 0xFFFFFFFF
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -71,6 +73,7 @@ def lib():
             "mtp_quantize_head_fp8": ([P, i32, i32, P, P, P, sz, P], ctypes.c_int),
             "mtp_draft_bf16": ([W, i32, P, P, P, P, P, sz, P], ctypes.c_int),
             "mtp_draft_fp8w": ([W, P, P, i32, P, P, P, P, P, sz, P], ctypes.c_int),
+            "mtp_draft_static": ([W, P, P, i32, P, P, P, P, P], ctypes.c_int),
             "mtp_front": ([W, i32, P, P, P, P, sz, P], ctypes.c_int),
             "mtp_head_bf16": ([W, i32, P, P, P, P, sz, P], ctypes.c_int),
             "mtp_head_fp8w": ([W, P, P, i32, P, P, P, P, sz, P], ctypes.c_int),
@@ -217,6 +220,25 @@ def mtp_draft_fp8w(w: mtp_weights, q, scale, batch: int, tokens, hidden, draft, 
     _check(lib().mtp_draft_fp8w(w.ref(), _dev(q, "q", torch.uint8, n),
                                 _dev(scale, "scale", torch.float32, w.vocab), batch, t, h, d, lg,
                                 ws, nws, _stream(stream)), "mtp_draft_fp8w")
+
+
+def mtp_draft_static(w: mtp_weights, q, scale, batch: int, tokens, hidden, draft, logits,
+                     stream=None) -> None:
+    """The allocation-free draft call: the BF16 head when q and scale are
+    None, else the FP8 copy; the library's static scratch replaces the
+    workspace (calls that overlap on one GPU race)."""
+    H, V = w.hidden, w.vocab
+    t = (_dev(tokens, "tokens", torch.int32, batch) if tokens.dtype == torch.int32
+         else _dev(tokens, "tokens", torch.uint32, batch))
+    d = (_dev(draft, "draft", torch.int32, batch) if draft.dtype == torch.int32
+         else _dev(draft, "draft", torch.uint32, batch))
+    n = V * H
+    _check(lib().mtp_draft_static(
+        w.ref(), _dev(q, "q", torch.uint8, n, optional=True),
+        _dev(scale, "scale", torch.float32, V, optional=True), batch, t,
+        _dev(hidden, "hidden", torch.bfloat16, batch * H), d,
+        _dev(logits, "logits", torch.bfloat16, batch * V, optional=True), _stream(stream)),
+        "mtp_draft_static")
 
 
 def mtp_front(w: mtp_weights, batch: int, tokens, hidden, x, workspace, stream=None) -> None:

@@ -2,13 +2,23 @@
 //
 // Host side only: argument validation (every host-visible error is returned
 // before anything is enqueued), workspace carving and kernel launches.  The
-// library keeps no state between calls.
+// only state kept between calls is the device address of the static scratch
+// of mtp_draft_static, per GPU.
+#include <mutex>
+
 #include "../../include/mtp_draft.h"
 #include "common.hpp"
 #include "kernels.hpp"
 #include "ctx_gemm.hpp"
 
 using namespace mtp;
+
+// Scratch of the allocation-free entry point (mtp_draft_static): the sweep's
+// workspace in a static device array, one copy per GPU the library runs on.
+// In host code this name stands for a host-side placeholder, not a device
+// address; only the address hipGetSymbolAddress returns may be handed to
+// kernels or runtime calls.
+static __device__ __align__(256) unsigned char scratch[MTP_STATIC_SCRATCH_BYTES];
 
 namespace {
 
@@ -278,6 +288,36 @@ int run_chain(const mtp_weights *w, bool fp8, const uint8_t *q, const float *sca
     return MTP_OK;
 }
 
+// The device address of `scratch` on `dev`, resolved on the first call for
+// that device with the device current (each GPU holds its own copy), then
+// kept.  MTP_ERR_HIP when the runtime cannot resolve it.
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch[kMaxDevices] = {};
+
+int static_scratch(int dev, void **out)
+{
+    if (dev < 0 || dev >= kMaxDevices)
+        return MTP_ERR_HIP;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch[dev]) {
+        int cur = 0;
+        if (hipGetDevice(&cur) != hipSuccess)
+            return MTP_ERR_HIP;
+        if (cur != dev && hipSetDevice(dev) != hipSuccess)
+            return MTP_ERR_HIP;
+        void *p = nullptr;
+        const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (cur != dev && hipSetDevice(cur) != hipSuccess)
+            return MTP_ERR_HIP;
+        if (e != hipSuccess || !p)
+            return MTP_ERR_HIP;
+        g_scratch[dev] = p;
+    }
+    *out = g_scratch[dev];
+    return MTP_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -334,6 +374,33 @@ int mtp_draft_fp8w(const mtp_weights *w, const uint8_t *q, const float *scale, i
 {
     return run_draft(w, true, q, scale, batch, tokens, hidden, draft, logits, workspace, ws_bytes,
                      stream);
+}
+
+int mtp_draft_static(const mtp_weights *w, const uint8_t *q, const float *scale, int32_t batch,
+                     const uint32_t *tokens, const void *hidden, uint32_t *draft, void *logits,
+                     void *stream)
+{
+    if (!w)
+        return MTP_ERR_NULL;
+    if ((q == nullptr) != (scale == nullptr))
+        return MTP_ERR_NULL;
+    const bool fp8 = q != nullptr;
+    MTP_TRY(check_shape(w->hidden, w->vocab, batch));
+    if (ws_layout(w->hidden, batch).total > MTP_STATIC_SCRATCH_BYTES)
+        return MTP_ERR_SCRATCH;
+    // every other argument is checked as for the draft calls; the scratch
+    // stands in for the workspace (a placeholder address: nothing is read)
+    MTP_TRY(validate_draft(w, fp8, q, scale, batch, tokens, hidden, draft, logits,
+                           reinterpret_cast<void *>(uintptr_t(256)), MTP_STATIC_SCRATCH_BYTES));
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    int dev = 0;
+    if (s ? hipStreamGetDevice(s, &dev) != hipSuccess : hipGetDevice(&dev) != hipSuccess)
+        return MTP_ERR_HIP;
+    void *ws = nullptr;
+    MTP_TRY(static_scratch(dev, &ws));
+    const WsLayout L = ws_layout(w->hidden, batch);
+    return run_sweep(w, fp8, q, scale, batch, tokens, hidden, ws_at(ws, L.x_off), draft, logits,
+                     ws, s);
 }
 
 size_t mtp_chain_workspace_bytes(int32_t hidden, int32_t vocab, int32_t batch)
@@ -472,6 +539,7 @@ const char *mtp_status_str(int status)
     case MTP_ERR_WORKSPACE: return "workspace missing or too small";
     case MTP_ERR_NONFINITE: return "a weight is NaN or Inf";
     case MTP_ERR_HIP: return "HIP runtime error";
+    case MTP_ERR_SCRATCH: return "shape needs more than the static scratch of mtp_draft_static";
     default: return "unknown status";
     }
 }

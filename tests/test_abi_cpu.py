@@ -35,7 +35,7 @@ def test_header_symbols_exported():
 
 
 def test_status_strings():
-    for code in range(7):
+    for code in range(8):
         assert mtp.mtp_status_str(code)
     assert mtp.mtp_status_str(99) == "unknown status"
 
@@ -163,3 +163,42 @@ def test_probe_argument_errors():
     assert L.mtp_probe_stream_read(P(0x1000), 1024, P(0x2000), 17, None) == mtp.MTP_ERR_SHAPE
     assert L.mtp_probe_stream_read(P(0x1008), 1024, P(0x2000), 2, None) == mtp.MTP_ERR_ALIGN
     assert L.mtp_probe_stream_read(P(0x1000), 1024, P(0x2002), 2, None) == mtp.MTP_ERR_ALIGN
+
+
+def test_static_entry_host_errors():
+    """The allocation-free call rejects shapes whose workspace exceeds its
+    static scratch, and bad arguments, before any device call."""
+    L = mtp.lib()
+    P = ctypes.c_void_p
+
+    def call(w, q=None, s=None, batch=2, tokens=0x90000, hidden=0xA0000, draft=0xB0000):
+        return L.mtp_draft_static(ctypes.byref(w) if w is not None else None,
+                                  P(q) if q else None, P(s) if s else None, batch,
+                                  P(tokens) if tokens else None, P(hidden) if hidden else None,
+                                  P(draft) if draft else None, None, None)
+    big = _fake_weights(H=8192, V=1000)
+    assert mtp.mtp_workspace_bytes(8192, 1000, 64) > mtp.MTP_STATIC_SCRATCH_BYTES
+    assert call(big, batch=64) == mtp.MTP_ERR_SCRATCH
+    assert mtp.mtp_workspace_bytes(6144, 154880, 32) <= mtp.MTP_STATIC_SCRATCH_BYTES
+    w = _fake_weights()
+    assert call(None) == mtp.MTP_ERR_NULL
+    assert call(w, q=0x70000) == mtp.MTP_ERR_NULL          # q without scale
+    assert call(w, s=0x80000) == mtp.MTP_ERR_NULL          # scale without q
+    assert call(w, tokens=0) == mtp.MTP_ERR_NULL
+    assert call(w, hidden=0xA0008) == mtp.MTP_ERR_ALIGN
+    assert call(w, batch=0) == mtp.MTP_ERR_SHAPE
+    assert call(_fake_weights(lm_head=0)) == mtp.MTP_ERR_NULL  # the BF16 head needs lm_head
+    assert "static scratch" in mtp.mtp_status_str(mtp.MTP_ERR_SCRATCH)
+
+
+def test_library_imports_no_allocator():
+    """No entry point can allocate: the library does not even import the HIP
+    runtime's allocation functions."""
+    import subprocess
+    out = subprocess.run(["nm", "-D", "--undefined-only", mtp.lib_path()], capture_output=True,
+                         text=True, check=True).stdout
+    syms = {ln.split()[-1] for ln in out.splitlines() if ln.strip()}
+    assert any(sym.startswith("hipLaunchKernel") or sym == "hipGetLastError" for sym in syms)
+    bad = [sym for sym in syms if sym.startswith(("hipMalloc", "hipFree", "hipHostMalloc",
+                                                  "hipHostFree", "hipExtMalloc", "hipMemAlloc"))]
+    assert not bad, bad
