@@ -44,6 +44,7 @@ struct MfmaArgs {
     int Ks;               // K columns per split (grid.y splits)
     int KC;               // K columns per LDS chunk (set by the launcher)
     int xs_off;           // LDS byte offset of the per-wave 2 KiB exchange scratch (launcher)
+    int spread;           // head: deal 16-row tiles across workgroups first (launcher)
     float *out_f32;       // EPI_STORE: [splits][B][N] FP32 partial sums
     uint16_t *logits;     // EPI_ARGMAX: [B][N] BF16 or null
     Partial *partials;    // EPI_ARGMAX: [B][kMaxHeadBlocks]

@@ -110,7 +110,11 @@ __global__ __launch_bounds__(WPB * 64) void mfma_gemm_kernel(MfmaArgs a)
     // streams one window of the matrix at a time: measured 3-7% faster than
     // 2048 waves each streaming its own region.
     const int Wt = gridDim.x * WPB;
-    const int gw = blockIdx.x * WPB + wid;
+    // The wave's slot in the grid.  Tiles go to slots in order (RR), so with
+    // fewer tiles than waves the slots are numbered across workgroups first:
+    // every CU then gets a share instead of the first workgroups all of it.
+    const int gw = (RR && a.spread) ? wid * int(gridDim.x) + int(blockIdx.x)
+                                    : int(blockIdx.x) * WPB + wid;
     const int R = (N + Wt - 1) / Wt;
     int r_lo = min(N, gw * R);
     int r_hi = min(N, r_lo + R);
@@ -527,19 +531,23 @@ hipError_t launch_eh_proj_mfma(const MfmaArgs &a_in, hipStream_t s)
 }
 
 // lm_head for B >= 2: one 8-wave workgroup per CU sharing the staged
-// activations; each wave streams an equal contiguous share of the rows.
+// activations; 16-row tiles dealt round-robin to the grid's waves.  Every CU
+// gets a workgroup as long as there is a tile for each (a vocabulary shard of
+// V/8 rows is 1210 tiles: 256 workgroups of 4-5 busy waves, where a floor of
+// 64 rows per wave had left 38 workgroups streaming it).
 hipError_t launch_head_mfma(const MfmaArgs &a_in, bool fp8, int *grid_out, hipStream_t s)
 {
     MfmaArgs a = a_in;
     a.Ks = a.K;
+    const int tiles = (a.N + 15) / 16;
     int grid = device_cu_count();
-    const int need = (a.N + 8 * 64 - 1) / (8 * 64);  // at least 64 rows per wave
-    if (grid > need)
-        grid = need;
+    if (grid > tiles)
+        grid = tiles;
     if (grid > kMaxHeadBlocks)
         grid = kMaxHeadBlocks;
     if (grid < 1)
         grid = 1;
+    a.spread = tiles < grid * 8;
     *grid_out = grid;
     return fp8 ? launch_mfma<true, EPI_ARGMAX, 8>(a, grid, 1, s)
                : launch_mfma<false, EPI_ARGMAX, 8>(a, grid, 1, s);
