@@ -22,7 +22,7 @@ __all__ = [
     "lib", "lib_path", "mtp_workspace_bytes", "mtp_validate_draft_args",
     "mtp_quantize_head_fp8", "mtp_draft_bf16", "mtp_draft_fp8w", "mtp_front", "mtp_head_bf16",
     "mtp_head_fp8w", "mtp_status_str", "new_workspace", "mtp_context_workspace_bytes",
-    "mtp_context_rows", "mtp_probe_stream_read", "mtp_draft_static",
+    "mtp_context_rows", "mtp_probe_stream_read", "mtp_probe_fp8_convert", "mtp_draft_static",
 ]
 
 MTP_OK, MTP_ERR_NULL, MTP_ERR_SHAPE, MTP_ERR_ALIGN = 0, 1, 2, 3
@@ -84,6 +84,7 @@ def lib():
             "mtp_draft_chain_bf16": ([W, i32, i32, P, P, P, P, P, sz, P], ctypes.c_int),
             "mtp_draft_chain_fp8w": ([W, P, P, i32, i32, P, P, P, P, P, sz, P], ctypes.c_int),
             "mtp_probe_stream_read": ([P, sz, P, i32, P], ctypes.c_int),
+            "mtp_probe_fp8_convert": ([P, P], ctypes.c_int),
         }
         for name, (args, res) in sigs.items():
             f = getattr(L, name)
@@ -344,3 +345,12 @@ def mtp_probe_stream_read(buf, out, wg_per_cu: int = 2, stream=None) -> None:
          else _dev(out, "out", torch.uint32, 1))
     _check(lib().mtp_probe_stream_read(ctypes.c_void_p(buf.data_ptr()), nbytes, o,
                                        int(wg_per_cu), _stream(stream)), "mtp_probe_stream_read")
+
+
+def mtp_probe_fp8_convert(result, stream=None) -> None:
+    """Check the hardware FP32 -> E4M3FN convert on every float of magnitude
+    <= 448; result (int32 or uint32 [2] device tensor) receives the number of
+    values whose code differs from round half to even, and the number checked."""
+    r = (_dev(result, "result", torch.int32, 2) if result.dtype == torch.int32
+         else _dev(result, "result", torch.uint32, 2))
+    _check(lib().mtp_probe_fp8_convert(r, _stream(stream)), "mtp_probe_fp8_convert")

@@ -1,8 +1,13 @@
-// probe.hip -- a plain streaming read of a device buffer, the practical
-// ceiling the weight sweeps are compared with: the same HBM, the same
-// 16-byte non-temporal loads, no arithmetic beyond folding the words read.
-// Consecutive lanes read consecutive 16-byte pieces (1 KiB per wave-wide
-// load), eight loads in flight per lane, grid-stride over the buffer.
+// probe.hip -- measurement and verification aids (include/mtp_probe.h).
+//
+// A plain streaming read of a device buffer, the practical ceiling the weight
+// sweeps are compared with: the same HBM, the same 16-byte non-temporal loads,
+// no arithmetic beyond folding the words read.  Consecutive lanes read
+// consecutive 16-byte pieces (1 KiB per wave-wide load), eight loads in flight
+// per lane, grid-stride over the buffer.
+//
+// A check of the hardware FP32 -> E4M3FN convert against round half to even
+// on every float of magnitude <= 448.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -40,8 +45,73 @@ __global__ __launch_bounds__(256) void stream_read_kernel(const u32x4p *__restri
         out[0] = acc;
 }
 
+// Nearest E4M3FN code of |y| <= 448, ties to the even code, sign kept, from
+// the binary32 bits: below 2^-6 the subnormal codes M = rint(|y| 2^9) (0..8;
+// 8 is the smallest normal, 0x08); above, the biased exponent and the 23-bit
+// mantissa rounded half to even to 3 bits (a carry moves into the exponent).
+__device__ __forceinline__ uint32_t e4m3_rne(float y)
+{
+    const uint32_t u = __float_as_uint(y);
+    const uint32_t sign = (u >> 24) & 0x80u;
+    const uint32_t mag = u & 0x7FFFFFFFu;
+    const uint32_t sub = uint32_t(__builtin_rintf(__uint_as_float(mag) * 512.0f));
+    const uint32_t e = (mag >> 23) - 127u + 7u;
+    const uint32_t m = mag & 0x7FFFFFu;
+    const uint32_t r = (m + 0x7FFFFu + ((m >> 20) & 1u)) >> 20;
+    return sign | (mag < 0x3C800000u ? sub : (e << 3) + r);
+}
+
+constexpr uint32_t kConvertTop = 0x43E00000u;  // 448.0f: bit patterns 0 .. this
+
+__global__ void convert_clear_kernel(uint32_t *res)
+{
+    res[0] = 0u;
+    res[1] = 0u;
+}
+
+// Thread i checks the floats with bits i and i | sign; the workgroup adds
+// its counts once.
+__global__ __launch_bounds__(256) void convert_check_kernel(uint32_t *res)
+{
+    const uint32_t i = blockIdx.x * 256u + threadIdx.x;
+    const bool in = i <= kConvertTop;
+    int bad = 0;
+    if (in) {
+#pragma unroll
+        for (uint32_t sg = 0; sg < 2; ++sg) {
+            const float x = __uint_as_float(i | (sg << 31));
+            const uint32_t hw =
+                uint32_t(__builtin_amdgcn_cvt_pk_fp8_f32(x, x, 0, false)) & 0xFFu;
+            bad += hw != e4m3_rne(x);
+        }
+    }
+    const int n_in = __syncthreads_count(in);
+    const int n_bad1 = __syncthreads_count(bad >= 1);
+    const int n_bad2 = __syncthreads_count(bad >= 2);
+    if (threadIdx.x == 0) {
+        atomicAdd(&res[1], uint32_t(2 * n_in));
+        if (n_bad1 + n_bad2)
+            atomicAdd(&res[0], uint32_t(n_bad1 + n_bad2));
+    }
+}
+
 }  // namespace
 }  // namespace mtp
+
+extern "C" int mtp_probe_fp8_convert(uint32_t *result, void *stream)
+{
+    if (!result)
+        return MTP_ERR_NULL;
+    if (reinterpret_cast<uintptr_t>(result) % 4 != 0)
+        return MTP_ERR_ALIGN;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipLaunchKernelGGL(mtp::convert_clear_kernel, dim3(1), dim3(1), 0, s, result);
+    if (hipGetLastError() != hipSuccess)
+        return MTP_ERR_HIP;
+    const uint32_t grid = (mtp::kConvertTop + 1u + 255u) / 256u;
+    hipLaunchKernelGGL(mtp::convert_check_kernel, dim3(grid), dim3(256), 0, s, result);
+    return hipGetLastError() == hipSuccess ? MTP_OK : MTP_ERR_HIP;
+}
 
 extern "C" int mtp_probe_stream_read(const void *buf, size_t bytes, uint32_t *out,
                                      int32_t wg_per_cu, void *stream)

@@ -163,6 +163,8 @@ def test_probe_argument_errors():
     assert L.mtp_probe_stream_read(P(0x1000), 1024, P(0x2000), 17, None) == mtp.MTP_ERR_SHAPE
     assert L.mtp_probe_stream_read(P(0x1008), 1024, P(0x2000), 2, None) == mtp.MTP_ERR_ALIGN
     assert L.mtp_probe_stream_read(P(0x1000), 1024, P(0x2002), 2, None) == mtp.MTP_ERR_ALIGN
+    assert L.mtp_probe_fp8_convert(None, None) == mtp.MTP_ERR_NULL
+    assert L.mtp_probe_fp8_convert(P(0x2002), None) == mtp.MTP_ERR_ALIGN
 
 
 def test_static_entry_host_errors():

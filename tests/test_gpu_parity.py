@@ -163,6 +163,18 @@ def test_stream_read_probe():
     assert int(out.item()) == 7
 
 
+def test_fp8_convert_probe():
+    """The hardware FP32 -> E4M3FN convert the quantiser encodes with rounds
+    to nearest, ties to even, on every float of magnitude <= 448."""
+    import mtp_draft_head_embed_amd as mtp
+    res = torch.full((2,), -1, dtype=torch.int32, device="cuda")
+    mtp.mtp_probe_fp8_convert(res)
+    torch.cuda.synchronize()
+    bad, checked = (int(v) for v in res.cpu().numpy().view(np.uint32))
+    assert checked == 2 * (0x43E00000 + 1)
+    assert bad == 0, bad
+
+
 def test_quantiser_nonfinite():
     import mtp_draft_head_embed_amd as mtp
     for bad in (0x7F80, 0xFF80, 0x7FC0):
