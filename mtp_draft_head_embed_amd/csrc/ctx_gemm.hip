@@ -27,6 +27,9 @@
 //     LDS accesses, with explicit waits that the MFMAs depend on: otherwise
 //     it waits for every load in flight before each read (it cannot tell
 //     that they fill other stages), and a fenced barrier would do the same;
+//   * a wave raises its priority while it issues its MFMAs, so the SIMD's
+//     arbiter prefers waves with matrix work ready over waves that are about
+//     to read LDS or wait (1-2% faster from T = 1024 to 16 384);
 //   * rows past T or H and columns past the split read zero (the buffer
 //     resource's range; an offset past it);
 //   * with few tiles (a skinny T) K is split over blockIdx.z so that the
@@ -214,6 +217,7 @@ __global__ __launch_bounds__(WM *WN * 64) void ctx_gemm_kernel(const uint16_t *_
             asm volatile("s_waitcnt lgkmcnt(3)" : "+v"(a[0]), "+v"(w[0]), "+v"(w[1]), "+v"(w[2]));
         else
             asm volatile("s_waitcnt lgkmcnt(3)" : "+v"(a[0]), "+v"(w[0]), "+v"(w[1]));
+        __builtin_amdgcn_s_setprio(1);
         mma_row(std::integral_constant<int, 0>{}, a[0], w);
         asm volatile("s_waitcnt lgkmcnt(2)" : "+v"(a[1]));
         mma_row(std::integral_constant<int, 1>{}, a[1], w);
@@ -221,6 +225,7 @@ __global__ __launch_bounds__(WM *WN * 64) void ctx_gemm_kernel(const uint16_t *_
         mma_row(std::integral_constant<int, 2>{}, a[2], w);
         asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(a[3]));
         mma_row(std::integral_constant<int, 3>{}, a[3], w);
+        __builtin_amdgcn_s_setprio(0);
     };
     auto compute = [&](const char *st) {
 #pragma unroll
