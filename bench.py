@@ -404,6 +404,32 @@ def main():
                              "frac_of_peak": round(head_bytes(H, Vs, B, fp8) / per / 1e9
                                                    / HBM_PEAK_GBPS, 4)}
             shards[f"G{G}"] = ent
+        if args.config == "large":
+            # the same shard shapes for the batched configuration's 16 sequences
+            # (the batched head on matrix cores)
+            btok16, bhid16 = synth.make_inputs(synth.CONFIGS["batched"])
+            xb = harness.to_dev_bf16(bhid16)
+            db = torch.empty(16, dtype=torch.int32, device=dev)
+            for G in (1, 2, 4, 8):
+                Vs = V // G
+                sw = mtp.mtp_weights(t["embed"][:Vs], t["enorm_w"], t["hnorm_w"], t["head_norm_w"],
+                                     t["eh_proj"], t["lm_head"][:Vs], float(wts["rms_eps"]))
+                slg = torch.empty((16, Vs), dtype=torch.bfloat16, device=dev)
+                sws = mtp.new_workspace(H, Vs, 16)
+                ent = {"rows": Vs, "batch": 16}
+                for name, fp8 in (("bf16", False), ("fp8", True)):
+                    def shead():
+                        if fp8:
+                            mtp.mtp_head_fp8w(sw, q[:Vs], s[:Vs], 16, xb, db, slg, sws, stream)
+                        else:
+                            mtp.mtp_head_bf16(sw, 16, xb, db, slg, sws, stream)
+                    g_s, _ = timed(shead, args.steps, args.warmup)
+                    per = g_s / args.steps
+                    ent[name] = {"head_us": round(per * 1e6, 2),
+                                 "GBps": round(head_bytes(H, Vs, 16, fp8) / per / 1e9, 1),
+                                 "frac_of_peak": round(head_bytes(H, Vs, 16, fp8) / per / 1e9
+                                                       / HBM_PEAK_GBPS, 4)}
+                shards[f"B16_G{G}"] = ent
         print(f"[bench] vocab shards: {shards}", file=sys.stderr, flush=True)
 
     batched = None
