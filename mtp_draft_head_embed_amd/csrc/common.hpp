@@ -119,6 +119,12 @@ __device__ __forceinline__ void wave_argmax(float &v, uint32_t &i)
 // ---------------------------------------------------------------------------
 // Vanilla RMSNorm pieces (x * w / sqrt(mean(x^2) + eps)) for one workgroup
 // holding one BF16 vector; thread t owns elements (i*blockDim + t)*8 .. +8.
+// The division by r is a multiplication by 1/r, correctly rounded once per
+// vector: x * w is exact in FP32 (BF16 x BF16), so each output before its
+// BF16 rounding is within about 31 units (2^-24) of the exact value (r itself
+// within 30: the sum of squares rounds at most 54 times over positive terms,
+// the square root halves that), against 30 with a division per element that
+// costs ten instructions.
 // ---------------------------------------------------------------------------
 // Sum of squares of a BF16 vector of n elements (n % 8 == 0,
 // n <= 4 * blockDim * 8), reduced over the whole workgroup in a fixed order.
@@ -159,6 +165,7 @@ __device__ __forceinline__ void norm_to_lds(const uint4 (&v)[4], const uint16_t 
                                             int n, float r, uint16_t *dst)
 {
     const int tid = threadIdx.x;
+    const float rr = 1.0f / r;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const int j = (i * blockDim.x + tid) * 8;
@@ -169,8 +176,8 @@ __device__ __forceinline__ void norm_to_lds(const uint4 (&v)[4], const uint16_t 
             uint32_t o[4];
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
-                const float lo = (bf16_lo(xa[q]) * bf16_lo(wa[q])) / r;
-                const float hi = (bf16_hi(xa[q]) * bf16_hi(wa[q])) / r;
+                const float lo = (bf16_lo(xa[q]) * bf16_lo(wa[q])) * rr;
+                const float hi = (bf16_hi(xa[q]) * bf16_hi(wa[q])) * rr;
                 o[q] = pack_bf16x2(lo, hi);
             }
             *reinterpret_cast<uint4 *>(dst + j) = make_uint4(o[0], o[1], o[2], o[3]);
@@ -251,8 +258,8 @@ __device__ __forceinline__ void dual_norm_store(const DualNormIn &v, int n, floa
         t0 += red[w];
         t1 += red[16 + w];
     }
-    const float r0 = sqrtf(t0 / float(n) + eps);
-    const float r1 = sqrtf(t1 / float(n) + eps);
+    const float rr0 = 1.0f / sqrtf(t0 / float(n) + eps);
+    const float rr1 = 1.0f / sqrtf(t1 / float(n) + eps);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const int j = (i * blockDim.x + tid) * 8;
@@ -264,10 +271,10 @@ __device__ __forceinline__ void dual_norm_store(const DualNormIn &v, int n, floa
             uint32_t oa[4], ob[4];
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
-                oa[q] = pack_bf16x2((bf16_lo(pa[q]) * bf16_lo(qa[q])) / r0,
-                                    (bf16_hi(pa[q]) * bf16_hi(qa[q])) / r0);
-                ob[q] = pack_bf16x2((bf16_lo(pb[q]) * bf16_lo(qb[q])) / r1,
-                                    (bf16_hi(pb[q]) * bf16_hi(qb[q])) / r1);
+                oa[q] = pack_bf16x2((bf16_lo(pa[q]) * bf16_lo(qa[q])) * rr0,
+                                    (bf16_hi(pa[q]) * bf16_hi(qa[q])) * rr0);
+                ob[q] = pack_bf16x2((bf16_lo(pb[q]) * bf16_lo(qb[q])) * rr1,
+                                    (bf16_hi(pb[q]) * bf16_hi(qb[q])) * rr1);
             }
             *reinterpret_cast<uint4 *>(dst0 + j) = make_uint4(oa[0], oa[1], oa[2], oa[3]);
             *reinterpret_cast<uint4 *>(dst1 + j) = make_uint4(ob[0], ob[1], ob[2], ob[3]);
@@ -324,7 +331,7 @@ __device__ __forceinline__ void single_norm_store(const SingleNormIn &v, int n, 
     float t0 = 0.f;
     for (int w2 = 0; w2 < nw; ++w2)
         t0 += red[w2];
-    const float r0 = sqrtf(t0 / float(n) + eps);
+    const float rr0 = 1.0f / sqrtf(t0 / float(n) + eps);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const int j = (i * blockDim.x + tid) * 8;
@@ -334,8 +341,8 @@ __device__ __forceinline__ void single_norm_store(const SingleNormIn &v, int n, 
             uint32_t oa[4];
 #pragma unroll
             for (int q = 0; q < 4; ++q)
-                oa[q] = pack_bf16x2((bf16_lo(pa[q]) * bf16_lo(qa[q])) / r0,
-                                    (bf16_hi(pa[q]) * bf16_hi(qa[q])) / r0);
+                oa[q] = pack_bf16x2((bf16_lo(pa[q]) * bf16_lo(qa[q])) * rr0,
+                                    (bf16_hi(pa[q]) * bf16_hi(qa[q])) * rr0);
             *reinterpret_cast<uint4 *>(dst + j) = make_uint4(oa[0], oa[1], oa[2], oa[3]);
         }
     }

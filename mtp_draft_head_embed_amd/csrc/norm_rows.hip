@@ -12,7 +12,7 @@
 
 namespace mtp {
 
-__global__ __launch_bounds__(512) void front_concat_kernel(FrontArgs a)
+__global__ __launch_bounds__(256) void front_concat_kernel(FrontArgs a)
 {
     __shared__ float red[32];
     const int b = blockIdx.x;
@@ -109,7 +109,7 @@ __global__ __launch_bounds__(512) void sum_norm_kernel(SumNormArgs a)
     float tot = 0.f;
     for (int w = 0; w < int(blockDim.x / kWave); ++w)
         tot += red[w];
-    const float r = sqrtf(tot / float(H) + a.eps);
+    const float rr = 1.0f / sqrtf(tot / float(H) + a.eps);  // as in the norms of common.hpp
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
         const int j = (i * blockDim.x + tid) * 8;
@@ -119,8 +119,8 @@ __global__ __launch_bounds__(512) void sum_norm_kernel(SumNormArgs a)
             uint32_t o[4];
 #pragma unroll
             for (int q = 0; q < 4; ++q)
-                o[q] = pack_bf16x2((bf16_lo(xa[q]) * bf16_lo(wa[q])) / r,
-                                   (bf16_hi(xa[q]) * bf16_hi(wa[q])) / r);
+                o[q] = pack_bf16x2((bf16_lo(xa[q]) * bf16_lo(wa[q])) * rr,
+                                   (bf16_hi(xa[q]) * bf16_hi(wa[q])) * rr);
             *reinterpret_cast<uint4 *>(a.xn_out + size_t(b) * H + j) =
                 make_uint4(o[0], o[1], o[2], o[3]);
         }
@@ -129,7 +129,9 @@ __global__ __launch_bounds__(512) void sum_norm_kernel(SumNormArgs a)
 
 hipError_t launch_front_concat(const FrontArgs &a, int batch, hipStream_t s)
 {
-    hipLaunchKernelGGL(front_concat_kernel, dim3(batch), dim3(512), 0, s, a);
+    // 256 threads x 4 pieces of 8 cover H <= 8192 (measured 1% faster than
+    // 512 threads for many rows)
+    hipLaunchKernelGGL(front_concat_kernel, dim3(batch), dim3(256), 0, s, a);
     return hipGetLastError();
 }
 

@@ -52,8 +52,9 @@ def bits_to_f64(b: np.ndarray) -> np.ndarray:
 # 6-level wave butterfly and at most 16 wave partials (all terms positive, so
 # <= 54 roundings relative to the sum); the mean, + eps and the correctly
 # rounded square root add 3, and the root halves the relative error: r is
-# within 30 units (2^-24) of its exact value; the product x_j w_j is exact
-# and the division adds one.  64 units leaves a margin.
+# within 30 units (2^-24) of its exact value; the product x_j w_j is exact,
+# and the library multiplies it by 1/r (one rounding for the reciprocal, one
+# for the product): within 32 units.  64 units leaves a margin.
 NORM_REL_ERR = 64 * 2.0 ** -24
 
 

@@ -21,24 +21,27 @@ def _rows(H, V, T, seed):
     return w, tokens, hiddens, oracle.context_rows(w, tokens, hiddens)
 
 
-def _fp32_norm(x_bits, w_bits, eps):
+def _fp32_norm(x_bits, w_bits, eps, recip=True):
     """BF16(x * w / sqrt(mean(x^2) + eps)) evaluated in float32 (numpy's
-    pairwise sum of squares), the way a GPU norm is computed."""
+    pairwise sum of squares), the way a GPU norm is computed: x * w times the
+    rounded reciprocal of the root (the library's form), or divided by it."""
     x = synth.from_bf16(x_bits)
     w = synth.from_bf16(w_bits)
     ss = np.sum(x * x, dtype=np.float32)
     r = np.sqrt(ss / np.float32(x.size) + np.float32(eps), dtype=np.float32)
+    if recip:
+        return synth.to_bf16((x * w) * (np.float32(1.0) / r))
     return synth.to_bf16((x * w) / r)
 
 
-def _fp32_concat(w, tokens, hiddens):
+def _fp32_concat(w, tokens, hiddens, recip=True):
     """The concat rows of the context rows (row r: tokens[r + 1], hiddens[r])
     with FP32 norms."""
     rows = []
     for r in range(hiddens.shape[0]):
         e = w["embed"][int(tokens[r + 1])]
-        rows.append(np.concatenate([_fp32_norm(e, w["enorm_w"], w["rms_eps"]),
-                                    _fp32_norm(hiddens[r], w["hnorm_w"], w["rms_eps"])]))
+        rows.append(np.concatenate([_fp32_norm(e, w["enorm_w"], w["rms_eps"], recip),
+                                    _fp32_norm(hiddens[r], w["hnorm_w"], w["rms_eps"], recip)]))
     return np.stack(rows)
 
 
@@ -65,13 +68,17 @@ def test_fp32_norm_flips_only_where_the_model_allows():
     the flip model marks (its unrounded value within the FP32 error of a BF16
     rounding boundary); and the model marks only a small share."""
     w, tokens, hiddens, ref = _rows(1024, 3000, 48, 85)
-    c32 = _fp32_concat(w, tokens, hiddens)
     delta = harness.concat_flip_delta(ref["concat"], ref["concat_unrounded"])
-    diff = c32 != ref["concat"]
-    assert np.all(delta[diff] > 0), np.argwhere(diff & (delta == 0))[:5]
-    # the flipped value is the neighbour the model names
-    assert np.all(np.abs(harness.bits_to_f64(c32) - harness.bits_to_f64(ref["concat"]))[diff]
-                  == delta[diff])
+    flipped = 0
+    for recip in (True, False):
+        c32 = _fp32_concat(w, tokens, hiddens, recip)
+        diff = c32 != ref["concat"]
+        flipped += int(diff.sum())
+        assert np.all(delta[diff] > 0), (recip, np.argwhere(diff & (delta == 0))[:5])
+        # the flipped value is the neighbour the model names
+        assert np.all(np.abs(harness.bits_to_f64(c32) - harness.bits_to_f64(ref["concat"]))[diff]
+                      == delta[diff])
+    assert flipped > 0  # the emulation does round some flagged entries the other way
     assert np.mean(delta > 0) < 0.01
 
 
