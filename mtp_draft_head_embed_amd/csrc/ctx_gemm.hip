@@ -77,7 +77,7 @@ __device__ __forceinline__ uint32_t lds_offset(const void *p)
 
 }  // namespace
 
-template <int BM, int BN, int WM, int WN, int BK = 32, int NST = 4>
+template <int BM, int BN, int WM, int WN, int BK = 32, int NST = 4, bool PREFETCH_A = true>
 __global__ __launch_bounds__(WM *WN * 64) void ctx_gemm_kernel(const uint16_t *__restrict__ A,
                                                                const uint16_t *__restrict__ W,
                                                                uint16_t *__restrict__ C,
@@ -229,10 +229,70 @@ __global__ __launch_bounds__(WM *WN * 64) void ctx_gemm_kernel(const uint16_t *_
         mma_row(std::integral_constant<int, 3>{}, a[3], w);
         __builtin_amdgcn_s_setprio(0);
     };
-    auto compute = [&](const char *st) {
+    // Two sub-steps: the second's A fragment i is read into a[i] as soon as
+    // the first's row i has issued its MFMAs (no extra registers), so those
+    // reads overlap the first sub-step's matrix work; only the second's W
+    // fragments wait in full.
+    auto compute2 = [&](const char *st) {
+        const uint32_t base = lds_offset(st);
+        u32x4_t a[FM], w[FN];
 #pragma unroll
-        for (int u = 0; u < NSUB; ++u)
-            compute_sub(st, aoff[u], woff[u]);
+        for (int j = 0; j < FN; ++j)
+            asm volatile("ds_read_b128 %0, %1" : "=v"(w[j]) : "v"(base + woff[0][j]));
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+            asm volatile("ds_read_b128 %0, %1" : "=v"(a[i]) : "v"(base + aoff[0][i]));
+        if constexpr (FN == 4)
+            asm volatile("s_waitcnt lgkmcnt(3)"
+                         : "+v"(a[0]), "+v"(w[0]), "+v"(w[1]), "+v"(w[2]), "+v"(w[3]));
+        else if constexpr (FN == 3)
+            asm volatile("s_waitcnt lgkmcnt(3)" : "+v"(a[0]), "+v"(w[0]), "+v"(w[1]), "+v"(w[2]));
+        else
+            asm volatile("s_waitcnt lgkmcnt(3)" : "+v"(a[0]), "+v"(w[0]), "+v"(w[1]));
+        __builtin_amdgcn_s_setprio(1);
+        // in flight before each row: the first sub-step's rows i..3 and the
+        // second's rows 0..i-1; reads complete in issue order
+        mma_row(std::integral_constant<int, 0>{}, a[0], w);
+        asm volatile("ds_read_b128 %0, %2\n\ts_waitcnt lgkmcnt(3)"
+                     : "=v"(a[0]), "+v"(a[1]) : "v"(base + aoff[1][0]));
+        mma_row(std::integral_constant<int, 1>{}, a[1], w);
+        asm volatile("ds_read_b128 %0, %2\n\ts_waitcnt lgkmcnt(3)"
+                     : "=v"(a[1]), "+v"(a[2]) : "v"(base + aoff[1][1]));
+        mma_row(std::integral_constant<int, 2>{}, a[2], w);
+        asm volatile("ds_read_b128 %0, %2\n\ts_waitcnt lgkmcnt(3)"
+                     : "=v"(a[2]), "+v"(a[3]) : "v"(base + aoff[1][2]));
+        mma_row(std::integral_constant<int, 3>{}, a[3], w);
+        asm volatile("ds_read_b128 %0, %1" : "=v"(a[3]) : "v"(base + aoff[1][3]));
+        __builtin_amdgcn_s_setprio(0);
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+            asm volatile("ds_read_b128 %0, %1" : "=v"(w[j]) : "v"(base + woff[1][j]));
+        if constexpr (FN == 4)
+            asm volatile("s_waitcnt lgkmcnt(0)"
+                         : "+v"(a[0]), "+v"(a[1]), "+v"(a[2]), "+v"(a[3]), "+v"(w[0]), "+v"(w[1]),
+                           "+v"(w[2]), "+v"(w[3]));
+        else if constexpr (FN == 3)
+            asm volatile("s_waitcnt lgkmcnt(0)"
+                         : "+v"(a[0]), "+v"(a[1]), "+v"(a[2]), "+v"(a[3]), "+v"(w[0]), "+v"(w[1]),
+                           "+v"(w[2]));
+        else
+            asm volatile("s_waitcnt lgkmcnt(0)"
+                         : "+v"(a[0]), "+v"(a[1]), "+v"(a[2]), "+v"(a[3]), "+v"(w[0]), "+v"(w[1]));
+        __builtin_amdgcn_s_setprio(1);
+        mma_row(std::integral_constant<int, 0>{}, a[0], w);
+        mma_row(std::integral_constant<int, 1>{}, a[1], w);
+        mma_row(std::integral_constant<int, 2>{}, a[2], w);
+        mma_row(std::integral_constant<int, 3>{}, a[3], w);
+        __builtin_amdgcn_s_setprio(0);
+    };
+    auto compute = [&](const char *st) {
+        if constexpr (NSUB == 2 && PREFETCH_A) {
+            compute2(st);
+        } else {
+#pragma unroll
+            for (int u = 0; u < NSUB; ++u)
+                compute_sub(st, aoff[u], woff[u]);
+        }
     };
 
     using I0 = std::integral_constant<int, 0>;
