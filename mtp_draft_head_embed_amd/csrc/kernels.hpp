@@ -91,6 +91,10 @@ hipError_t launch_front_concat(const FrontArgs &a, int batch, hipStream_t s);
 hipError_t launch_sum_norm(const SumNormArgs &a, int batch, hipStream_t s);
 hipError_t launch_eh_proj_mfma(const MfmaArgs &a, hipStream_t s);
 hipError_t launch_head_mfma(const MfmaArgs &a, bool fp8, int *grid_out, hipStream_t s);
+// lm_head for 2 <= B <= 16 at H <= 6144: one 16-row tile per workgroup at a
+// time, K split over its waves (head_tile.hip).
+bool head_tile_fits(int B, int K, bool fp8);
+hipError_t launch_head_tile(const MfmaArgs &a, bool fp8, int *grid_out, hipStream_t s);
 hipError_t launch_argmax_final(const Partial *partials, int nparts, const uint32_t *tokens,
                                int vocab, uint32_t *draft, int batch, hipStream_t s);
 

@@ -3,10 +3,14 @@ variant the launcher picks, against the FP64 oracle.
 
 The batched head streams lm_head once for all B sequences; which kernel runs
 depends on B and H only:
-  * batch tiles of 16 sequences: one (B <= 16), two (17-32), three (33-48)
-    or four (49-64), each with its own accumulators;
-  * K-chunked ("multi-chunk") head when B staged activation rows of H
-    columns do not fit in LDS: at H = 6144 from B = 12, at H = 8192 from B = 9;
+  * 2 <= B <= 16 at H <= 6144: the tile kernel (head_tile.hip), one 16-row
+    tile per workgroup with K split over its 8 waves; the wave's slice of each
+    row is 2, 4 or 6 segments of 128 bytes per chunk, one chunk (FP8, and BF16
+    to H = 3072) or two (BF16 above);
+  * otherwise batch tiles of 16 sequences: one (B <= 16), two (17-32), three
+    (33-48) or four (49-64), each with its own accumulators, K-chunked
+    ("multi-chunk") when B staged activation rows of H columns do not fit in
+    LDS: at H = 6144 from B = 17 (two tiles), at H = 8192 from B = 9;
   * K-chunked split-K eh_proj: at H = 6144 from B = 50, at H = 8192 from B = 28.
 V = 20 011 keeps the oracle cheap (the choice of kernel does not depend on V)
 and leaves a ragged last row tile.
@@ -34,13 +38,15 @@ V_CASE = 20011
 
 CASES = [
     # (H, B, seed, what the launcher runs)
-    (6144, 12, 201, "K-chunked head, one batch tile"),
-    (6144, 16, 202, "K-chunked head, one batch tile (the batched configuration's B)"),
+    (6144, 12, 201, "tile kernel, 6-segment chunks (BF16 two per tile)"),
+    (6144, 16, 202, "tile kernel at the batched configuration's B"),
+    (4096, 6, 212, "tile kernel, 4-segment chunks (BF16 two per tile)"),
+    (3088, 2, 213, "tile kernel, ragged last slice (BF16 7 of 8 segments)"),
     (6144, 17, 203, "K-chunked head, two batch tiles"),
     (6144, 33, 204, "K-chunked head, three batch tiles"),
     (6144, 50, 205, "K-chunked head, four tiles; first K-chunked split-K eh_proj"),
     (6144, 64, 206, "K-chunked head, four tiles; K-chunked eh_proj (largest batch)"),
-    (8192, 9, 207, "K-chunked head from B = 9 at the largest hidden"),
+    (8192, 9, 207, "K-chunked one-tile head from B = 9 at the largest hidden"),
     (8192, 28, 208, "K-chunked head, two tiles; K-chunked eh_proj at the largest hidden"),
     (2048, 17, 209, "single-chunk head, two batch tiles"),
     (1024, 48, 210, "single-chunk head, three batch tiles"),
