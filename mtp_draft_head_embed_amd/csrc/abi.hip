@@ -128,8 +128,11 @@ RowGemvArgs front_args(const mtp_weights *w, const uint32_t *tokens, const void 
 
 char *ws_at(void *ws, size_t off) { return static_cast<char *>(ws) + off; }
 
-// Batched front half: concat rows, eh_proj on MFMA with split-K partial sums,
+// Batched front half: eh_proj over the concat rows with split-K partial sums,
 // then x = BF16(sum of splits) and, when xn is wanted, the head norm of x.
+// For 2 <= B <= 16 at H a multiple of 1024 up to 6144 one kernel gathers,
+// normalises and multiplies (4 splits); otherwise the concat rows are written
+// first and eh_proj runs on the split-K MFMA kernel.
 int run_front_batched(const mtp_weights *w, int32_t batch, const uint32_t *tokens,
                       const void *hidden, void *x, void *xn, void *ws, hipStream_t s)
 {
@@ -144,21 +147,31 @@ int run_front_batched(const mtp_weights *w, int32_t batch, const uint32_t *token
     f.enorm_w = static_cast<const uint16_t *>(w->enorm_w);
     f.hnorm_w = static_cast<const uint16_t *>(w->hnorm_w);
     f.eps = w->rms_eps;
-    f.concat = reinterpret_cast<uint16_t *>(ws_at(ws, L.concat_off));
-    if (launch_front_concat(f, batch, s) != hipSuccess)
-        return MTP_ERR_HIP;
-    MfmaArgs m{};
-    m.W = w->eh_proj;
-    m.N = H;
-    m.K = 2 * H;
-    m.A = f.concat;
-    m.B = batch;
-    m.out_f32 = reinterpret_cast<float *>(ws_at(ws, L.p_off));
-    if (launch_eh_proj_mfma(m, s) != hipSuccess)
-        return MTP_ERR_HIP;
+    float *P = reinterpret_cast<float *>(ws_at(ws, L.p_off));
+    int splits;
+    if (front_tile_fits(batch, H)) {
+        if (launch_front_tile(f, static_cast<const uint16_t *>(w->eh_proj), P, batch, s) !=
+            hipSuccess)
+            return MTP_ERR_HIP;
+        splits = front_tile_splits();
+    } else {
+        f.concat = reinterpret_cast<uint16_t *>(ws_at(ws, L.concat_off));
+        if (launch_front_concat(f, batch, s) != hipSuccess)
+            return MTP_ERR_HIP;
+        MfmaArgs m{};
+        m.W = w->eh_proj;
+        m.N = H;
+        m.K = 2 * H;
+        m.A = f.concat;
+        m.B = batch;
+        m.out_f32 = P;
+        if (launch_eh_proj_mfma(m, s) != hipSuccess)
+            return MTP_ERR_HIP;
+        splits = eh_split(H).S;
+    }
     SumNormArgs r{};
-    r.P = m.out_f32;
-    r.S = eh_split(H).S;
+    r.P = P;
+    r.S = splits;
     r.B = batch;
     r.H = H;
     r.x_out = static_cast<uint16_t *>(x);

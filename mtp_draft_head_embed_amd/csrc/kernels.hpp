@@ -92,9 +92,16 @@ hipError_t launch_sum_norm(const SumNormArgs &a, int batch, hipStream_t s);
 hipError_t launch_eh_proj_mfma(const MfmaArgs &a, hipStream_t s);
 hipError_t launch_head_mfma(const MfmaArgs &a, bool fp8, int *grid_out, hipStream_t s);
 // lm_head for 2 <= B <= 16 at H <= 6144: one 16-row tile per workgroup at a
-// time, K split over its waves (head_tile.hip).
+// time, K split over its waves (tile_gemm.hip).
 bool head_tile_fits(int B, int K, bool fp8);
 hipError_t launch_head_tile(const MfmaArgs &a, bool fp8, int *grid_out, hipStream_t s);
+// eh_proj with the gather and both norms for 2 <= B <= 16 at H a multiple of
+// 1024 up to 6144: partial sums of front_tile_splits() K splits to
+// P[split][b][row] (tile_gemm.hip).
+bool front_tile_fits(int B, int H);
+int front_tile_splits();
+hipError_t launch_front_tile(const FrontArgs &f, const uint16_t *eh_proj, float *P, int batch,
+                             hipStream_t s);
 hipError_t launch_argmax_final(const Partial *partials, int nparts, const uint32_t *tokens,
                                int vocab, uint32_t *draft, int batch, hipStream_t s);
 

@@ -11,7 +11,11 @@ depends on B and H only:
     (33-48) or four (49-64), each with its own accumulators, K-chunked
     ("multi-chunk") when B staged activation rows of H columns do not fit in
     LDS: at H = 6144 from B = 17 (two tiles), at H = 8192 from B = 9;
-  * K-chunked split-K eh_proj: at H = 6144 from B = 50, at H = 8192 from B = 28.
+  * K-chunked split-K eh_proj: at H = 6144 from B = 50, at H = 8192 from B = 28;
+  * 2 <= B <= 16 at H a multiple of 1024 up to 6144: eh_proj in the tile
+    kernel with the gather and both norms in its prologue (K split in four,
+    H / 1024 segments per wave slice); other shapes write the concat rows
+    first and run the split-K MFMA eh_proj.
 V = 20 011 keeps the oracle cheap (the choice of kernel does not depend on V)
 and leaves a ragged last row tile.
 
@@ -41,7 +45,11 @@ CASES = [
     (6144, 12, 201, "tile kernel, 6-segment chunks (BF16 two per tile)"),
     (6144, 16, 202, "tile kernel at the batched configuration's B"),
     (4096, 6, 212, "tile kernel, 4-segment chunks (BF16 two per tile)"),
-    (3088, 2, 213, "tile kernel, ragged last slice (BF16 7 of 8 segments)"),
+    (3088, 2, 213, "tile kernel, ragged last slice (BF16 7 of 8 segments); concat-first front"),
+    (1024, 3, 214, "fused front, 1 segment per slice"),
+    (2048, 7, 215, "fused front, 2 segments per slice"),
+    (3072, 16, 216, "fused front, 3 segments per slice"),
+    (5120, 11, 217, "fused front, 5 segments per slice"),
     (6144, 17, 203, "K-chunked head, two batch tiles"),
     (6144, 33, 204, "K-chunked head, three batch tiles"),
     (6144, 50, 205, "K-chunked head, four tiles; first K-chunked split-K eh_proj"),

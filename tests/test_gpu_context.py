@@ -51,6 +51,7 @@ def _run(H, V, T, seed, bad_row=None, sample=None):
     (256, 3000, 65, 84), (256, 3000, 200, 85), (1040, 2000, 65, 86), (1040, 2000, 130, 87),
     (512, 4000, 300, 88), (1040, 2000, 600, 94), (256, 3000, 255, 95), (256, 3000, 256, 96),
     (1040, 2000, 40, 98), (256, 3000, 128, 97), (256, 3000, 129, 99),
+    (2048, 3000, 16, 101),  # 2..16 rows at H a multiple of 1024: the fused front
 ])
 def test_context_rows(H, V, T, seed):
     _run(H, V, T, seed)
@@ -60,6 +61,7 @@ def test_context_rows_out_of_range_token():
     """A row whose token is out of range leaves the other rows exact."""
     _run(256, 3000, 100, 89, bad_row=41)
     _run(256, 3000, 10, 90, bad_row=3)
+    _run(1024, 3000, 9, 102, bad_row=4)  # the fused front (gather in its prologue)
 
 
 @pytest.mark.slow

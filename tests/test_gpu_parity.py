@@ -192,11 +192,13 @@ def test_quantiser_nonfinite():
     mtp.mtp_quantize_head_fp8(harness.to_dev_bf16(rows), 5, 32, q, s, ws)
 
 
-def test_invalid_tokens_and_no_logits():
+@pytest.mark.parametrize("H", [512, 1024])
+def test_invalid_tokens_and_no_logits(H):
     """tokens >= V give MTP_DRAFT_INVALID for that sequence only; skipping the
-    logits output leaves the drafts unchanged."""
-    _say("\n[invalid tokens]")
-    cfg = synth.custom(512, 3000, 4, 40)
+    logits output leaves the drafts unchanged (H = 512: the concat rows are
+    written first; H = 1024: the fused front gathers in its prologue)."""
+    _say(f"\n[invalid tokens] H={H}")
+    cfg = synth.custom(H, 3000, 4, 40)
     wts = synth.make_weights(cfg)
     tokens, hidden = synth.make_inputs(cfg)
     tokens[1] = 3000

@@ -75,11 +75,10 @@ def test_oracle_threads_under_thread_sanitizer(tmp_path):
 
 @pytest.mark.skipif(not os.path.exists(HIPCC), reason="hipcc not installed")
 def test_abi_host_layer_under_address_and_ub_sanitizers(tmp_path):
-    build = os.path.join(ROOT, "mtp_draft_head_embed_amd", "_build")
-    others = [os.path.join(build, f + ".o") for f in
-              ("row_gemv", "quant", "mfma_gemm", "norm_rows", "probe", "ctx_gemm")]
+    from mtp_draft_head_embed_amd import build as hip_build
+    others = [os.path.join(hip_build.BUILD_DIR, os.path.splitext(f)[0] + ".o")
+              for f in hip_build.SOURCES if f != "abi.hip"]
     if not all(os.path.exists(o) for o in others):
-        from mtp_draft_head_embed_amd import build as hip_build
         hip_build.build()
     abi_o = str(tmp_path / "abi_san.o")
     rc, out = _run([HIPCC, "--offload-arch=gfx950", "-O1", "-g", "-std=c++17", "-fPIC",
