@@ -28,6 +28,9 @@
 //     LDS accesses, with explicit waits that the MFMAs depend on: otherwise
 //     it waits for every load in flight before each read (it cannot tell
 //     that they fill other stages), and a fenced barrier would do the same;
+//   * on 64-column steps the second 32-column sub-step's A fragments are read
+//     into each register as soon as the first sub-step's MFMAs that use it
+//     have issued, so only the W fragment reads are waited for in full;
 //   * a wave raises its priority while it issues its MFMAs, so the SIMD's
 //     arbiter prefers waves with matrix work ready over waves that are about
 //     to read LDS or wait (1-2% faster from T = 1024 to 16 384);
