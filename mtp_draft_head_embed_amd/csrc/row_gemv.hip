@@ -11,7 +11,7 @@
 //     LDS) and the first argmax stage (`argmax_bf16`) as the epilogue: every
 //     logit is rounded to BF16 and optionally stored, and each workgroup leaves
 //     its best (value, index) in a partials array; argmax_final_kernel, one
-//     workgroup per sequence, reduces them.  (A last-workgroup-done fusion of
+//     wavefront per sequence, reduces them.  (A last-workgroup-done fusion of
 //     the two stages needs agent-scope release/acquire, which on gfx950 writes
 //     back and invalidates the XCD's whole L2 in every workgroup: measured at
 //     +35-55 us per sweep, against 1-3 us for the second launch.)
@@ -320,55 +320,68 @@ __global__ __launch_bounds__(BS) void row_gemv_kernel(RowGemvArgs a)
     }
 }
 
-// Second argmax stage: one workgroup per sequence reduces its partials and
+// Second argmax stage: one wavefront per sequence reduces its partials and
 // writes the draft (MTP_DRAFT_INVALID when the sequence's token is out of
-// range).
-__global__ __launch_bounds__(256) void argmax_final_kernel(const Partial *__restrict__ partials,
-                                                           int nparts, const uint32_t *tokens,
-                                                           int vocab, uint32_t *draft)
+// range).  One wave needs no LDS and no barrier: eight partials per lane are
+// loaded before any is compared (one memory latency per 512 partials, which
+// covers the heads' grids), each 16-lane row is reduced with DPP moves, and
+// the four row winners are compared in row order from v_readlane.  The
+// (value, lower index) order is total, so any reduction tree picks the same
+// winner.  (A 256-thread workgroup with LDS-permute butterflies took 4.5 us
+// per call.)
+__global__ __launch_bounds__(64) void argmax_final_kernel(const Partial *__restrict__ partials,
+                                                          int nparts, const uint32_t *tokens,
+                                                          int vocab, uint32_t *draft)
 {
-    __shared__ float sv[4];
-    __shared__ uint32_t si[4];
     const int b = blockIdx.x;
-    const int tid = threadIdx.x;
+    const int lane = threadIdx.x;
     // the token check's load (every lane reads the same word) goes out
     // together with the partials' loads and is used only at the end
     const uint32_t tk = tokens ? tokens[b] : 0u;
     float bv = -INFINITY;
     uint32_t bi = 0xFFFFFFFFu;
-    // four partials per thread are loaded before any is compared (one memory
-    // latency per batch, not per partial); a slot past nparts re-reads the
-    // last partial and is skipped.  The (value, lower index) order is
-    // associative, so the batching does not change the result.
-    constexpr int PER = 4;
-    for (int p0 = tid; p0 < nparts; p0 += PER * int(blockDim.x)) {
+    // a slot past nparts re-reads the last partial and is skipped
+    constexpr int PER = 8;
+    for (int p0 = lane; p0 < nparts; p0 += PER * kWave) {
         Partial q[PER];
 #pragma unroll
         for (int u = 0; u < PER; ++u)
-            q[u] = partials[size_t(b) * kMaxHeadBlocks + min(p0 + u * int(blockDim.x), nparts - 1)];
+            q[u] = partials[size_t(b) * kMaxHeadBlocks + min(p0 + u * kWave, nparts - 1)];
 #pragma unroll
         for (int u = 0; u < PER; ++u)
-            if (p0 + u * int(blockDim.x) < nparts && better(q[u].val, q[u].idx, bv, bi)) {
+            if (p0 + u * kWave < nparts && better(q[u].val, q[u].idx, bv, bi)) {
                 bv = q[u].val;
                 bi = q[u].idx;
             }
     }
-    wave_argmax(bv, bi);
-    if ((tid & (kWave - 1)) == 0) {
-        sv[tid / kWave] = bv;
-        si[tid / kWave] = bi;
+    auto step = [&](auto ctrl) {
+        constexpr int C = decltype(ctrl)::value;
+        const float ov = __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(bv), C, 0xF, 0xF, false));
+        const uint32_t oi = uint32_t(__builtin_amdgcn_mov_dpp(int(bi), C, 0xF, 0xF, false));
+        if (better(ov, oi, bv, bi)) {
+            bv = ov;
+            bi = oi;
+        }
+    };
+    step(std::integral_constant<int, 0xB1>{});   // quad_perm [1, 0, 3, 2]
+    step(std::integral_constant<int, 0x4E>{});   // quad_perm [2, 3, 0, 1]
+    step(std::integral_constant<int, 0x141>{});  // row_half_mirror
+    step(std::integral_constant<int, 0x140>{});  // row_mirror
+    float rv = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(bv), 0));
+    uint32_t ri = uint32_t(__builtin_amdgcn_readlane(int(bi), 0));
+#pragma unroll
+    for (int r = 1; r < 4; ++r) {
+        const float v = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(bv), 16 * r));
+        const uint32_t i = uint32_t(__builtin_amdgcn_readlane(int(bi), 16 * r));
+        if (better(v, i, rv, ri)) {
+            rv = v;
+            ri = i;
+        }
     }
-    __syncthreads();
-    if (tid == 0) {
-        // wave 0's result is already in (bv, bi)
-        for (int w = 1; w < int(blockDim.x / kWave); ++w)
-            if (better(sv[w], si[w], bv, bi)) {
-                bv = sv[w];
-                bi = si[w];
-            }
+    if (lane == 0) {
         if (tokens && tk >= uint32_t(vocab))
-            bi = 0xFFFFFFFFu;
-        draft[b] = bi;
+            ri = 0xFFFFFFFFu;
+        draft[b] = ri;
     }
 }
 
@@ -476,7 +489,7 @@ hipError_t launch_head(const RowGemvArgs &a, bool fp8, int batch, hipStream_t s)
 hipError_t launch_argmax_final(const Partial *partials, int nparts, const uint32_t *tokens,
                                int vocab, uint32_t *draft, int batch, hipStream_t s)
 {
-    hipLaunchKernelGGL(argmax_final_kernel, dim3(batch), dim3(256), 0, s, partials, nparts,
+    hipLaunchKernelGGL(argmax_final_kernel, dim3(batch), dim3(kWave), 0, s, partials, nparts,
                        tokens, vocab, draft);
     return hipGetLastError();
 }
