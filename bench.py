@@ -519,6 +519,22 @@ def main():
                     HBM_PEAK_GBPS * 1e9) else "hbm",
                 "roofline_frac": round(t_roof / per, 3),
             }
+        # The vendor library on the same product (torch's BF16 matmul, which
+        # runs hipBLASLt): the GEMM alone, with the weight pre-transposed so no
+        # transposed view reaches it.  A reference point for ctx_gemm_kernel,
+        # not part of the path.
+        wt = dw.tensors["eh_proj"].t().contiguous()
+        lib_gemm = {}
+        for T in (1024, 4096):
+            a = torch.randn(T, 2 * H, device=dev).to(torch.bfloat16)
+            n = max(10, min(args.steps, 20))
+            g_s, _ = timed(lambda: torch.matmul(a, wt), n, max(2, min(args.warmup, 5)))
+            per = g_s / n
+            lib_gemm[f"T{T}"] = {"us_per_call": round(per * 1e6, 2),
+                                 "TFLOPs": round(2.0 * T * H * 2 * H / per / 1e12, 1)}
+            del a
+        del wt
+        context["library_gemm"] = lib_gemm
         print(f"[bench] context rows: {context}", file=sys.stderr, flush=True)
 
     agreement = None
