@@ -104,9 +104,9 @@ __global__ __launch_bounds__(512) void tile_gemm_kernel(TileArgs a)
     //   head: tile t0 + i G to workgroup t0.  Workgroups are dispatched to the
     //   8 XCDs in turn, each XCD with its own L2, and are numbered here XCD by
     //   XCD: neighbouring tiles then go to one XCD, so the 32-byte logit pieces
-    //   they write into one 128-byte line meet in one L2 (numbered in dispatch
-    //   order, the logits cost the B = 16 head another 14 us (FP8) and 22 us
-    //   (BF16) at V = 154 880).
+    //   they write into one 128-byte line meet in one L2 (measured while the
+    //   logits were stored tile by tile: numbered in dispatch order, they cost
+    //   the B = 16 head another 15 us (FP8) and 22 us (BF16) at V = 154 880).
     //   front: workgroup w takes K split w % 4 of tiles w / 4 + i G / 4, so its
     //   A fragments (one split) serve all its tiles.
     int t0, tstride, split = 0;
