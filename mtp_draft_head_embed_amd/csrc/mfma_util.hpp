@@ -1,5 +1,5 @@
 // mfma_util.hpp -- operand helpers shared by the matrix-core kernels of the
-// batched sweep (mfma_gemm.hip, head_tile.hip).  Internal to the library.
+// batched sweep (mfma_gemm.hip, tile_gemm.hip).  Internal to the library.
 #pragma once
 
 #include <hip/hip_runtime.h>

@@ -86,7 +86,10 @@ __global__ __launch_bounds__(512) void tile_gemm_kernel(TileArgs a)
     __shared__ __attribute__((aligned(16))) char xs_all[8 * 2048];
     __shared__ f32x4 red[2][8][kWave];
     __shared__ __attribute__((aligned(16))) OutT ob[NBUF][16][16];
-    __shared__ float rrs[16];  // front: 1 / r of each sequence's half
+    // front: the split's half of the 16 normed rows, rows padded by 16 bytes
+    // so that the 16 lanes of a fragment read hit distinct banks
+    constexpr int XLS = NSEG * 512 + 8;
+    __shared__ __attribute__((aligned(16))) uint16_t xl[HEAD ? 8 : 16 * XLS];
 
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
@@ -176,44 +179,45 @@ __global__ __launch_bounds__(512) void tile_gemm_kernel(TileArgs a)
     } else {
         // The split lies in one half of [enorm(e) | hnorm(h)]: hf = 0, the
         // embedding row of the sequence's token (zero for a token outside the
-        // vocabulary); hf = 1, its hidden row.  Loads complete in issue order,
-        // so the norm's row loads go out first, then the first weight chunk,
-        // then the slice loads for the fragments, then the second chunk: each
-        // wait below then covers only what it needs.
+        // vocabulary); hf = 1, its hidden row.  Wave w loads the whole rows of
+        // sequences w and w + 8 (rows past B repeat row B - 1) for their sums
+        // of squares, norms the split's half of them (x * w exact, times 1 / r
+        // once per row, as the norms of common.hpp do) into LDS, and after a
+        // barrier every wave reads its fragments from there.  Loads complete in
+        // issue order: the tokens first (one wait), then the rows and the norm
+        // weight, then the first weight chunk; the LDS writes go out before the
+        // second chunk.
         const int H = N;
         const int hf = split / 2;
         const uint16_t *nw = hf ? a.hnorm_w : a.enorm_w;
-        // every row address first: the embedding half's three token loads go
-        // out together before any other load, so one wait covers them and no
-        // later wait for a token also waits for a weight chunk (the hidden
-        // half, a workgroup-uniform branch, loads none)
-        const int ms[3] = {min(wid, B - 1), min(wid + 8, B - 1), arow};
-        uint32_t tk[3] = {0u, 0u, 0u};
-        if (!hf) {
+        const int ms[2] = {min(wid, B - 1), min(wid + 8, B - 1)};
+        uint32_t tk[2] = {0u, 0u};
+        if (!hf) {  // workgroup-uniform; the hidden half needs no token
 #pragma unroll
-            for (int i = 0; i < 3; ++i)
+            for (int i = 0; i < 2; ++i)
                 tk[i] = a.tokens[ms[i]];
         }
-        bool ok[3];
-        const uint16_t *rows[3];
+        bool sok[2];
+        const uint16_t *srow[2];
 #pragma unroll
-        for (int i = 0; i < 3; ++i) {
-            ok[i] = hf || tk[i] < uint32_t(a.vocab);
-            rows[i] = hf ? a.hidden + size_t(ms[i]) * size_t(H)
-                         : a.embed + (ok[i] ? size_t(tk[i]) * size_t(H) : size_t(0));
+        for (int i = 0; i < 2; ++i) {
+            sok[i] = hf || tk[i] < uint32_t(a.vocab);
+            srow[i] = hf ? a.hidden + size_t(ms[i]) * size_t(H)
+                         : a.embed + (sok[i] ? size_t(tk[i]) * size_t(H) : size_t(0));
         }
-        const bool sok[2] = {ok[0], ok[1]}, aok = ok[2];
-        const uint16_t *srow[2] = {rows[0], rows[1]};
-        const uint16_t *src = rows[2];
-        // sums of squares: wave w takes sequences w and w + 8 (rows past B
-        // repeat row B - 1), 2 NSEG 16-byte pieces of each per lane
+        // 16-byte piece p of a row holds columns (p * 64 + lane) * 8 ..; the
+        // split's H / 2 columns of the half are pieces p0 .. p0 + NSEG - 1
         constexpr int PPL = 2 * NSEG;  // H / 512
-        uint4 sv[2][PPL];
+        const int p0 = (split % 2) * NSEG;
+        uint4 sv[2][PPL], wv[NSEG];
 #pragma unroll
         for (int i = 0; i < 2; ++i)
 #pragma unroll
             for (int p = 0; p < PPL; ++p)
                 sv[i][p] = *reinterpret_cast<const uint4 *>(srow[i] + (p * kWave + lane) * 8);
+#pragma unroll
+        for (int p = 0; p < NSEG; ++p)
+            wv[p] = *reinterpret_cast<const uint4 *>(nw + ((p0 + p) * kWave + lane) * 8);
         load_chunk(rA, 0, 0);
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
@@ -227,35 +231,40 @@ __global__ __launch_bounds__(512) void tile_gemm_kernel(TileArgs a)
                     ss = fmaf(bf16_hi(w4[e]), bf16_hi(w4[e]), ss);
                 }
             }
-            ss = sok[i] ? wave_sum(ss) : 0.f;
-            if (lane == 0)
-                rrs[wid + 8 * i] = 1.0f / sqrtf(ss / float(H) + a.eps);  // as the norms of common.hpp
+            ss = wave_sum(ss);
+            const float rr = 1.0f / sqrtf(ss / float(H) + a.eps);  // as the norms of common.hpp
+            uint16_t *dst = xl + (wid + 8 * i) * XLS;
+#pragma unroll
+            for (int p = 0; p < NSEG; ++p) {
+                // both indices compile-time and the choice made per component:
+                // a runtime index, or a choice between the two elements, would
+                // move sv to scratch memory
+                const bool odd = split & 1;
+                const uint4 hi = sv[i][NSEG + p], lo = sv[i][p];
+                const uint4 xv = make_uint4(odd ? hi.x : lo.x, odd ? hi.y : lo.y, odd ? hi.z : lo.z,
+                                            odd ? hi.w : lo.w);
+                const uint32_t x4[4] = {xv.x, xv.y, xv.z, xv.w};
+                const uint32_t w4[4] = {wv[p].x, wv[p].y, wv[p].z, wv[p].w};
+                uint32_t o[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    o[e] = sok[i] ? pack_bf16x2((bf16_lo(x4[e]) * bf16_lo(w4[e])) * rr,
+                                                (bf16_hi(x4[e]) * bf16_hi(w4[e])) * rr)
+                                  : 0u;
+                *reinterpret_cast<uint4 *>(dst + (p * kWave + lane) * 8) =
+                    make_uint4(o[0], o[1], o[2], o[3]);
+            }
         }
-        // the fragments' slice of the sequence's row and of the norm weight
-        uint4 xv[NA], wv[NA];
+        load_chunk(rB, 1, 0);
+        asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");  // the normed rows
+        // fragment (s, q): columns frag_col(s, q) - the split's first column
+        const int cbase = split * (K / kFrontSplits);
 #pragma unroll
         for (int s = 0; s < NSEG; ++s)
 #pragma unroll
-            for (int q = 0; q < SPS; ++q) {
-                const int c = frag_col(s, q) - hf * H;
-                xv[s * SPS + q] = *reinterpret_cast<const uint4 *>(src + c);
-                wv[s * SPS + q] = *reinterpret_cast<const uint4 *>(nw + c);
-            }
-        load_chunk(rB, 1, 0);
-        asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");  // rrs
-        const float rr = rrs[arow];
-#pragma unroll
-        for (int i = 0; i < NA; ++i) {
-            const uint32_t x4[4] = {xv[i].x, xv[i].y, xv[i].z, xv[i].w};
-            const uint32_t w4[4] = {wv[i].x, wv[i].y, wv[i].z, wv[i].w};
-            uint32_t o[4];
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-                o[e] = aok ? pack_bf16x2((bf16_lo(x4[e]) * bf16_lo(w4[e])) * rr,
-                                         (bf16_hi(x4[e]) * bf16_hi(w4[e])) * rr)
-                           : 0u;
-            af[i] = make_uint4(o[0], o[1], o[2], o[3]);
-        }
+            for (int q = 0; q < SPS; ++q)
+                af[s * SPS + q] =
+                    *reinterpret_cast<const uint4 *>(xl + arow * XLS + (frag_col(s, q) - cbase));
     }
 
     // Multiply chunk C (compile-time) into acc.
