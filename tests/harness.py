@@ -177,7 +177,9 @@ def run_draft(dw: DevWeights, tokens: np.ndarray, hidden: np.ndarray, fp8=None,
     tk = torch.from_numpy(tokens.astype(np.uint32).view(np.int32)).to(device)
     hd = to_dev_bf16(hidden.reshape(B, dw.hidden), device)
     dr = torch.empty(B, dtype=torch.int32, device=device)
-    lg = torch.empty((B, dw.vocab), dtype=torch.bfloat16, device=device) if with_logits else None
+    # NaN-filled, so a logit the call leaves unwritten fails every comparison
+    lg = (torch.full((B, dw.vocab), float("nan"), dtype=torch.bfloat16, device=device)
+          if with_logits else None)
     ws = mtp.new_workspace(dw.hidden, dw.vocab, B, device)
     if fp8 is None:
         mtp.mtp_draft_bf16(dw.w, B, tk, hd, dr, lg, ws)
