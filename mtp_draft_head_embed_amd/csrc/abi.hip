@@ -178,12 +178,15 @@ int run_front_batched(const mtp_weights *w, int32_t batch, const uint32_t *token
     r.norm_w = static_cast<const uint16_t *>(w->head_norm_w);
     r.eps = w->rms_eps;
     r.xn_out = static_cast<uint16_t *>(xn);
+    r.zero_ctr = reinterpret_cast<uint32_t *>(ws_at(ws, L.ctr_off));
     if (launch_sum_norm(r, batch, s) != hipSuccess)
         return MTP_ERR_HIP;
     return MTP_OK;
 }
 
 // Batched head: lm_head on MFMA over the normed xn, then the final argmax.
+// Always launched right after a sum_norm on the same stream, which clears the
+// head's tile counter in the workspace.
 int run_head_batched(const mtp_weights *w, bool fp8, const uint8_t *q, const float *scale,
                      int32_t batch, const void *xn, const uint32_t *tokens, uint32_t *draft,
                      void *logits, void *ws, hipStream_t s)
@@ -198,6 +201,7 @@ int run_head_batched(const mtp_weights *w, bool fp8, const uint8_t *q, const flo
     m.B = batch;
     m.logits = static_cast<uint16_t *>(logits);
     m.partials = reinterpret_cast<Partial *>(ws_at(ws, L.part_off));
+    m.tile_ctr = reinterpret_cast<uint32_t *>(ws_at(ws, L.ctr_off));  // cleared by sum_norm
     int grid = 0;
     if (launch_head_mfma(m, fp8, &grid, s) != hipSuccess)
         return MTP_ERR_HIP;
@@ -221,6 +225,7 @@ int run_head(const mtp_weights *w, bool fp8, const uint8_t *q, const float *scal
         r.norm_w = static_cast<const uint16_t *>(w->head_norm_w);
         r.eps = w->rms_eps;
         r.xn_out = reinterpret_cast<uint16_t *>(ws_at(ws, L.xn_off));
+        r.zero_ctr = reinterpret_cast<uint32_t *>(ws_at(ws, L.ctr_off));
         if (launch_sum_norm(r, batch, s) != hipSuccess)
             return MTP_ERR_HIP;
         return run_head_batched(w, fp8, q, scale, batch, r.xn_out, tokens, draft, logits, ws, s);

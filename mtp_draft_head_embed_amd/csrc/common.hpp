@@ -29,10 +29,17 @@ struct Partial {
 
 inline size_t align256(size_t n) { return (n + 255) & ~size_t(255); }
 
+// The batched head deals its last tiles from kTilePools counters in the
+// workspace, each on its own 4 KiB (so that they sit in different memory
+// channels and their atomics do not queue behind one another).
+constexpr int kTilePools = 8;
+constexpr int kCtrStride = 4096;
+
 struct WsLayout {
     size_t x_off, x_bytes;
     size_t part_off, part_bytes;
     size_t concat_off, xn_off, p_off;
+    size_t ctr_off;  // the batched head's tile counters, kTilePools of them kCtrStride bytes apart
     size_t total;
 };
 
@@ -56,6 +63,8 @@ inline WsLayout ws_layout(int hidden, int batch)
     } else {
         L.concat_off = L.xn_off = L.p_off = 0;
     }
+    L.ctr_off = L.total;
+    L.total += size_t(kTilePools) * kCtrStride;
     return L;
 }
 

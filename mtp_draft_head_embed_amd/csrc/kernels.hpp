@@ -48,6 +48,7 @@ struct MfmaArgs {
     float *out_f32;       // EPI_STORE: [splits][B][N] FP32 partial sums
     uint16_t *logits;     // EPI_ARGMAX: [B][N] BF16 or null
     Partial *partials;    // EPI_ARGMAX: [B][kMaxHeadBlocks]
+    uint32_t *tile_ctr;   // EPI_ARGMAX: the tile head's kTilePools counters, zero at launch (sum_norm clears them)
 };
 
 // eh_proj K-split for the batched path: S splits of Ks columns.
@@ -74,6 +75,7 @@ struct SumNormArgs {
     const uint16_t *norm_w;
     float eps;
     uint16_t *xn_out;     // [B][H] BF16 normed x, or null
+    uint32_t *zero_ctr;   // when not null: the tile counters of the head launched next, set to zero
 };
 
 int device_cu_count();

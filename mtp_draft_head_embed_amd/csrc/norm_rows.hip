@@ -31,6 +31,8 @@ __global__ __launch_bounds__(512) void sum_norm_kernel(SumNormArgs a)
     const int b = blockIdx.x;
     const int H = a.H;
     const int tid = threadIdx.x;
+    if (a.zero_ctr && b == 0 && tid < kTilePools)
+        a.zero_ctr[tid * (kCtrStride / 4)] = 0u;
     if (a.S == 0) {
         single_norm(a.x_in + size_t(b) * H, a.norm_w, H, a.eps, a.xn_out + size_t(b) * H, red);
         return;

@@ -54,6 +54,7 @@ struct TileArgs {
     const uint16_t *A;    // [B][K] BF16 normed activations
     uint16_t *logits;     // [B][N] BF16 or null
     Partial *partials;    // [B][kMaxHeadBlocks]
+    uint32_t *tile_ctr;   // kTilePools counters kCtrStride bytes apart, zero at launch
     // front (K = 2H, N = H)
     const uint16_t *embed;
     int vocab;
@@ -90,6 +91,9 @@ __global__ __launch_bounds__(512) void tile_gemm_kernel(TileArgs a)
     // so that the 16 lanes of a fragment read hit distinct banks
     constexpr int XLS = NSEG * 512 + 8;
     __shared__ __attribute__((aligned(16))) uint16_t xl[HEAD ? 8 : 16 * XLS];
+    // head: the tile of the workgroup's s-th slot at s % 128 (outlives the
+    // NBUF slots whose outputs wait in ob)
+    __shared__ int slot_tile[HEAD ? 128 : 1];
 
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
@@ -103,13 +107,24 @@ __global__ __launch_bounds__(512) void tile_gemm_kernel(TileArgs a)
     const int T16 = (N + 15) / 16;
     const int G = int(gridDim.x);
 
-    // Tiles to workgroups.
-    //   head: tile t0 + i G to workgroup t0.  Workgroups are dispatched to the
-    //   8 XCDs in turn, each XCD with its own L2, and are numbered here XCD by
-    //   XCD: neighbouring tiles then go to one XCD, so the 32-byte logit pieces
-    //   they write into one 128-byte line meet in one L2 (measured while the
-    //   logits were stored tile by tile: numbered in dispatch order, they cost
-    //   the B = 16 head another 15 us (FP8) and 22 us (BF16) at V = 154 880).
+    // Tiles to workgroups.  A tile at or past T16 is empty: its loads read
+    // zero without touching memory and it stores nothing.
+    //   head: slot s < RS of workgroup w holds tile t0 + s G.  Workgroups are
+    //   dispatched to the 8 XCDs in turn, each XCD with its own L2, and are
+    //   numbered here XCD by XCD, so neighbouring tiles meet in one L2
+    //   (measured while the logits were stored tile by tile: numbered in
+    //   dispatch order, they cost the B = 16 head another 15 us (FP8) and
+    //   22 us (BF16) at V = 154 880).  The last three to four rounds of tiles,
+    //   from RS G on, are dealt on demand instead: the XCDs do not stream
+    //   equally fast (at V = 154 880, B = 16 FP8: 3.11 us per tile on half of
+    //   them, 3.35 on the other half), and with fixed shares the slower half
+    //   finished 8 us after the faster.  They form P pools, pool p holding
+    //   tiles RS G + p + P i, shared by the workgroups w with (w / 8) mod P = p
+    //   (four per XCD at G = 256); a workgroup's next tile in its pool is the
+    //   count its pool's counter held when it added one.  One counter for all
+    //   tiles, taken about 75 times per us, did not keep up (the B = 16 FP8
+    //   sweep took 213 us against 181); P counters on their own 4 KiB pages,
+    //   taken only in the tail, do.
     //   front: workgroup w takes K split w % 4 of tiles w / 4 + i G / 4, so its
     //   A fragments (one split) serve all its tiles.
     int t0, tstride, split = 0;
@@ -122,21 +137,45 @@ __global__ __launch_bounds__(512) void tile_gemm_kernel(TileArgs a)
         t0 = int(blockIdx.x) / kFrontSplits;
         tstride = G / kFrontSplits;
     }
-    const int ntile = (T16 - 1 - t0) / tstride + 1;  // >= 1: the grid has no idle workgroup
-    // the workgroup's tix-th tile; from ntile on, tiles at or past T16
-    auto tile_of = [&](int tix) { return t0 + tix * tstride; };
+    // front: the workgroup's tix-th tile (>= 1 tile: the grid has no idle workgroup)
+    const int ntile = (T16 - 1 - t0) / tstride + 1;
+    auto tile_of = [&](int tix) {
+        if constexpr (HEAD)
+            return __builtin_amdgcn_readfirstlane(slot_tile[tix & 127]);
+        else
+            return t0 + tix * tstride;
+    };
+    // head: static slots, pools, this workgroup's pool
+    const int RS = max(2, T16 / G - 3);
+    const int npool = max(1, min(kTilePools, G / 8));
+    const int pool = (int(blockIdx.x) / 8) % npool;
+    const __amdgpu_buffer_rsrc_t ctr_rs = __builtin_amdgcn_make_buffer_rsrc(
+        HEAD ? a.tile_ctr : nullptr, 0, HEAD ? kTilePools * kCtrStride : 0, kBufFlags);
+    // Slot s's tile, for s >= 2.  Every lane issues the atomic (no branch, so
+    // the loads around it are counted exactly); only thread 0's, and only for
+    // a pooled slot, lies inside the counters' range, every other one outside
+    // it, which touches no memory.  Thread 0 gets the count back; publish()
+    // turns it into the tile.
+    auto take = [&](int s) {
+        const bool real = tid == 0 && s >= RS;
+        return uint32_t(__builtin_amdgcn_raw_ptr_buffer_atomic_add_i32(
+            1, ctr_rs, real ? pool * kCtrStride : int(0x80000000u), 0, 0));
+    };
+    auto publish = [&](int s, uint32_t g) {  // thread 0: slot s's tile into slot_tile
+        if (tid == 0)
+            slot_tile[s & 127] = s < RS ? t0 + s * G : RS * G + pool + npool * int(g);
+    };
     // the wave's slice of each row (bytes): head, wave w of the whole row;
     // front, wave w of the split's H / 2 columns (H = 1024 NSEG: SB bytes)
     const int sb0 = HEAD ? wid * SB : (split * (K / kFrontSplits)) * 2 + wid * SB;
 
-    // Chunk c of tile `tix` (the workgroup's tix-th tile): load u reads rows
-    // 0-7 (u even) or 8-15 (u odd) of segment u / 2, 16 bytes per lane.  Rows
-    // past N lie outside the resource and columns past K are sent outside it:
-    // both read zero.  A tile at or past the last (tix >= ntile: rows from N
-    // on) gets an empty range, so its loads read zero without touching memory;
-    // the loop below issues them unconditionally.
-    auto load_chunk = [&](uint4 (&raw)[NL], int tix, int c) {
-        const int r0 = min(N, tile_of(tix) * 16);
+    // Chunk c of a tile: load u reads rows 0-7 (u even) or 8-15 (u odd) of
+    // segment u / 2, 16 bytes per lane.  Rows past N lie outside the resource
+    // and columns past K are sent outside it: both read zero.  An empty tile
+    // (rows from N on) gets an empty range, so its loads read zero without
+    // touching memory; the loops below issue them unconditionally.
+    auto load_chunk = [&](uint4 (&raw)[NL], int tile, int c) {
+        const int r0 = min(N, tile * 16);
         const int r1 = min(N, r0 + 16);
         const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
             const_cast<char *>(Wb) + size_t(r0) * size_t(rowb), 0, (r1 - r0) * rowb, kBufFlags);
@@ -218,7 +257,7 @@ __global__ __launch_bounds__(512) void tile_gemm_kernel(TileArgs a)
 #pragma unroll
         for (int p = 0; p < NSEG; ++p)
             wv[p] = *reinterpret_cast<const uint4 *>(nw + ((p0 + p) * kWave + lane) * 8);
-        load_chunk(rA, 0, 0);
+        load_chunk(rA, tile_of(0), 0);
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
             float ss = 0.f;
@@ -255,7 +294,7 @@ __global__ __launch_bounds__(512) void tile_gemm_kernel(TileArgs a)
                     make_uint4(o[0], o[1], o[2], o[3]);
             }
         }
-        load_chunk(rB, 1, 0);
+        load_chunk(rB, tile_of(1), 0);
         asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");  // the normed rows
         // fragment (s, q): columns frag_col(s, q) - the split's first column
         const int cbase = split * (K / kFrontSplits);
@@ -302,10 +341,10 @@ __global__ __launch_bounds__(512) void tile_gemm_kernel(TileArgs a)
     // n = (t / 4) % 16.
     const int m_out = 4 * (tid >> 6) + (tid & 3);
     const int n_out = (tid >> 2) & 15;
-    auto load_scale = [&](int tix) {
+    auto load_scale = [&](int tile) {
         float sc = 1.0f;
-        if (HEAD && FP8 && wid < 4 && tix < ntile) {
-            const int row = tile_of(tix) * 16 + n_out;
+        if (HEAD && FP8 && wid < 4) {
+            const int row = tile * 16 + n_out;
             if (row < N)
                 sc = a.scale[row];
         }
@@ -326,8 +365,8 @@ __global__ __launch_bounds__(512) void tile_gemm_kernel(TileArgs a)
                 return;
             for (int pc = tid; pc < (f1 - f0) * 32; pc += 512) {
                 const int tix = f0 + (pc >> 5), m = (pc >> 1) & 15, h = pc & 1;
-                const int r0 = tile_of(tix) * 16 + 8 * h;
-                if (m < B && tix < ntile && r0 < N) {
+                const int r0 = slot_tile[tix & 127] * 16 + 8 * h;
+                if (m < B && r0 < N) {
                     const uint16_t *src = &ob[tix % NBUF][m][8 * h];
                     uint16_t *dst = a.logits + size_t(m) * N + r0;
                     if (r0 + 8 <= N && (N & 7) == 0) {
@@ -343,13 +382,13 @@ __global__ __launch_bounds__(512) void tile_gemm_kernel(TileArgs a)
             for (int pc = tid; pc < (f1 - f0) * 64; pc += 512) {
                 const int tix = f0 + (pc >> 6), m = (pc >> 2) & 15, qd = pc & 3;
                 const int r0 = tile_of(tix) * 16 + 4 * qd;
-                if (m < B && tix < ntile)
+                if (m < B && r0 < N)
                     *reinterpret_cast<float4 *>(a.out_f32 + (size_t(split) * B + m) * N + r0) =
                         *reinterpret_cast<const float4 *>(&ob[tix % NBUF][m][4 * qd]);
             }
         }
     };
-    auto finish = [&](f32x4 &acc, int tix, float sc) {
+    auto finish = [&](f32x4 &acc, int tix, int tile, float sc) {
         const int p = tix & 1;
         red[p][wid][lane] = acc;
         acc = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -366,7 +405,7 @@ __global__ __launch_bounds__(512) void tile_gemm_kernel(TileArgs a)
 #pragma unroll
             for (int w = 0; w < 8; ++w)
                 z += rf[w * 4 * kWave + tid];
-            const uint32_t row = uint32_t(tile_of(tix) * 16 + n_out);
+            const uint32_t row = uint32_t(tile * 16 + n_out);
             if (row < uint32_t(N) && m_out < B) {
                 if constexpr (HEAD) {
                     const uint32_t lb = f32_to_bf16_bits(FP8 ? z * sc : z);
@@ -389,46 +428,92 @@ __global__ __launch_bounds__(512) void tile_gemm_kernel(TileArgs a)
     // memory operations (scale loads) before it: a stricter count then only
     // waits for those older operations, never for the chunk just prefetched.
     f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
-    if constexpr (CH == 1) {
-        // tiles alternate between the two buffers; an odd count ends with an
-        // empty tile (zero loads, nothing stored).  The front issued its first
-        // two chunks in the prologue.
-        float scA = load_scale(0);
-        if constexpr (HEAD)
-            load_chunk(rA, 0, 0);
-        float scB = load_scale(1);
-        if constexpr (HEAD)
-            load_chunk(rB, 1, 0);
+    int nslot;  // slots run (the last may hold an empty tile)
+    if constexpr (!HEAD) {
+        // tiles alternate between the two buffers, issued in the prologue; an
+        // odd count ends with an empty tile
 #pragma unroll 1
         for (int t = 0; t < ntile; t += 2) {
             compute(rA, acc, std::integral_constant<int, 0>{});
-            finish(acc, t, scA);
-            scA = load_scale(t + 2);
-            load_chunk(rA, t + 2, 0);
+            finish(acc, t, tile_of(t), 1.0f);
+            load_chunk(rA, tile_of(t + 2), 0);
             compute(rB, acc, std::integral_constant<int, 0>{});
-            finish(acc, t + 1, scB);
-            scB = load_scale(t + 3);
-            load_chunk(rB, t + 3, 0);
+            finish(acc, t + 1, tile_of(t + 1), 1.0f);
+            load_chunk(rB, tile_of(t + 3), 0);
         }
-    } else {
-        // chunk 0 of every tile in rA, chunk 1 in rB
-        float sc = load_scale(0);
-        load_chunk(rA, 0, 0);
-        load_chunk(rB, 0, 1);
+        nslot = ntile;
+    } else if constexpr (CH == 1) {
+        // Slots alternate between the two buffers.  Slot s + 2's tile is taken
+        // when slot s - 2 is done, published before slot s's barrier and read
+        // after it, when its chunk is issued: a count comes back while two
+        // tiles stream.  The slots' tiles increase, so the first empty one
+        // ends the loop.  Each take is issued before the chunk it precedes, so
+        // the wait for that chunk covers it.
+        int tA = t0, tB = t0 + G;
+        if (tid == 0) {
+            slot_tile[0] = tA;
+            slot_tile[1] = tB;
+        }
+        uint32_t gA = take(2);
+        float scA = load_scale(tA);
+        load_chunk(rA, tA, 0);
+        float scB = load_scale(tB);
+        uint32_t gB = take(3);
+        load_chunk(rB, tB, 0);
+        int t = 0;
 #pragma unroll 1
-        for (int t = 0; t < ntile; ++t) {
+        for (; tA < T16; t += 2) {
             compute(rA, acc, std::integral_constant<int, 0>{});
-            load_chunk(rA, t + 1, 0);
-            compute(rB, acc, std::integral_constant<int, 1>{});
-            finish(acc, t, sc);
-            sc = load_scale(t + 1);
-            load_chunk(rB, t + 1, 1);
+            publish(t + 2, gA);
+            finish(acc, t, tA, scA);
+            tA = tile_of(t + 2);
+            scA = load_scale(tA);
+            gA = take(t + 4);
+            load_chunk(rA, tA, 0);
+            compute(rB, acc, std::integral_constant<int, 0>{});
+            publish(t + 3, gB);
+            finish(acc, t + 1, tB, scB);
+            tB = tile_of(t + 3);
+            scB = load_scale(tB);
+            gB = take(t + 5);
+            load_chunk(rB, tB, 0);
         }
+        nslot = t;
+    } else {
+        // Chunk 0 of every slot in rA, chunk 1 in rB.  Slot s + 2's tile is
+        // taken when slot s - 1 is done, published before slot s's barrier and
+        // read after it, a slot before its chunks are issued.
+        int tc = t0, tn = t0 + G;  // this slot's tile, the next one's
+        if (tid == 0) {
+            slot_tile[0] = tc;
+            slot_tile[1] = tn;
+        }
+        // the take between the two chunks, where each step issues it (the
+        // compiler keeps the smaller count where the paths into the loop meet)
+        float sc = load_scale(tc);
+        load_chunk(rA, tc, 0);
+        uint32_t g = take(2);
+        load_chunk(rB, tc, 1);
+        int t = 0;
+#pragma unroll 1
+        for (; tc < T16; ++t) {
+            compute(rA, acc, std::integral_constant<int, 0>{});
+            load_chunk(rA, tn, 0);
+            compute(rB, acc, std::integral_constant<int, 1>{});
+            publish(t + 2, g);
+            finish(acc, t, tc, sc);
+            sc = load_scale(tn);
+            g = take(t + 3);
+            load_chunk(rB, tn, 1);
+            tc = tn;
+            tn = tile_of(t + 2);
+        }
+        nslot = t;
     }
 
     // the outputs still in LDS
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-    flush((ntile - 1) / NBUF * NBUF, ntile);
+    flush((nslot - 1) / NBUF * NBUF, nslot);
 
     if constexpr (HEAD) {
         // Per sequence, the best of the workgroup: the 16 threads of sequence
@@ -482,6 +567,9 @@ hipError_t launch_head_tile(const MfmaArgs &m, bool fp8, int *grid_out, hipStrea
     a.A = m.A;
     a.logits = m.logits;
     a.partials = m.partials;
+    a.tile_ctr = m.tile_ctr;
+    if (!a.tile_ctr)
+        return hipErrorInvalidValue;
     const int tiles = (a.N + 15) / 16;
     int grid = device_cu_count();
     if (grid > tiles)

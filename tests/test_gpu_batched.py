@@ -128,3 +128,29 @@ def test_batched_variant(H, B, seed, what):
                                     wts["eh_proj"])
     _say(f"[batched] H={H} B={B}: {len(picks)} sequences against the oracle, worst logit error "
          f"{worst['bf16']:.3f} tol (BF16) / {worst['fp8']:.3f} tol (FP8); x: {st}")
+
+
+@pytest.mark.parametrize("V,B,seed", [(300, 4, 221), (4099, 9, 222)])
+def test_tile_head_small_vocab(V, B, seed):
+    """Vocabularies with fewer 16-row tiles than two grid rounds: the grid is one
+    workgroup per tile (V = 300: 19 of them, so fewer than eight tile pools, and
+    every pool empty) or one per CU with the second round partly empty
+    (V = 4 099: 257 tiles, the last holding 3 rows).  Every logit of every
+    sequence, both heads, against the oracle."""
+    _say(f"\n[batched] small vocabulary H=1024 V={V} B={B} seed={seed}")
+    cfg = synth.custom(1024, V, B, seed, distinct_tokens=True)
+    wts = synth.make_weights(cfg)
+    tokens, hidden = synth.make_inputs(cfg)
+    dw = harness.upload(wts)
+    q, s = harness.quantize_dev(dw)
+    ref = oracle.quantize_fp8(wts["lm_head"])
+    d16, lg16 = harness.run_draft(dw, tokens, hidden)
+    d8, lg8 = harness.run_draft(dw, tokens, hidden, fp8=(q, s))
+    _self_consistent(d16, lg16)
+    _self_consistent(d8, lg8)
+    for b in range(B):
+        for d, lg, fp8 in ((d16, lg16, None), (d8, lg8, ref)):
+            r = oracle.draft(wts, int(tokens[b]), hidden[b], fp8=fp8)
+            rep = harness.compare_sequence(b, r["o"], lg[b], int(d[b]), r["draft"],
+                                           harness.TOL_FP8 if fp8 is not None else harness.TOL_BF16)
+            assert rep.ok, (fp8 is not None, rep)
