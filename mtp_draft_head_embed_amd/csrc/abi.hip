@@ -186,7 +186,7 @@ int run_front_batched(const mtp_weights *w, int32_t batch, const uint32_t *token
 
 // Batched head: lm_head on MFMA over the normed xn, then the final argmax.
 // Always launched right after a sum_norm on the same stream, which clears the
-// head's tile counter in the workspace.
+// head's tile counters in the workspace.
 int run_head_batched(const mtp_weights *w, bool fp8, const uint8_t *q, const float *scale,
                      int32_t batch, const void *xn, const uint32_t *tokens, uint32_t *draft,
                      void *logits, void *ws, hipStream_t s)

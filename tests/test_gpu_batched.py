@@ -130,12 +130,13 @@ def test_batched_variant(H, B, seed, what):
          f"{worst['bf16']:.3f} tol (BF16) / {worst['fp8']:.3f} tol (FP8); x: {st}")
 
 
-@pytest.mark.parametrize("V,B,seed", [(300, 4, 221), (4099, 9, 222)])
+@pytest.mark.parametrize("V,B,seed", [(300, 4, 221), (4099, 9, 222), (20, 16, 223)])
 def test_tile_head_small_vocab(V, B, seed):
     """Vocabularies with fewer 16-row tiles than two grid rounds: the grid is one
     workgroup per tile (V = 300: 19 of them, so fewer than eight tile pools, and
-    every pool empty) or one per CU with the second round partly empty
-    (V = 4 099: 257 tiles, the last holding 3 rows).  Every logit of every
+    every pool empty), one per CU with the second round partly empty
+    (V = 4 099: 257 tiles, the last holding 3 rows), or fewer tiles than
+    sequences (V = 20: 2 tiles, B = 16; two workgroups).  Every logit of every
     sequence, both heads, against the oracle."""
     _say(f"\n[batched] small vocabulary H=1024 V={V} B={B} seed={seed}")
     cfg = synth.custom(1024, V, B, seed, distinct_tokens=True)
