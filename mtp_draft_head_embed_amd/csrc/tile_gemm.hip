@@ -9,8 +9,9 @@
 //     in the prologue, FP32 partial sums out (H a multiple of 1024 up to 6144).
 //
 // Work split.  16-row tiles of the weight matrix are dealt round-robin to the
-// workgroups (one 8-wave workgroup per CU), and the 8 waves split each tile's
-// K (or the workgroup's K split) into 8 equal slices.  A workgroup therefore
+// workgroups (one 8-wave workgroup per CU; the head's last three to four
+// rounds on demand instead, from counters in the workspace), and the 8 waves
+// split each tile's K (or the workgroup's K split) into 8 equal slices.  A workgroup therefore
 // reads 16 whole rows (or row quarters) at a time, and the grid a window of
 // 256 such blocks: a streaming probe reads 12 KiB rows 8% faster this way than
 // with one tile per wave (7.15 against 6.63 TB/s), 6 KiB rows about 1% faster.
