@@ -210,10 +210,12 @@ int run_head_batched(const mtp_weights *w, bool fp8, const uint8_t *q, const flo
     return MTP_OK;
 }
 
-// The head sweep from a block output x: norm, lm_head, argmax.
+// The head sweep from a block output x: norm, lm_head, argmax.  row_ctr (one
+// sequence): the workspace's row counters, cleared by the eh_proj launched
+// just before; null deals every row round-robin.
 int run_head(const mtp_weights *w, bool fp8, const uint8_t *q, const float *scale, int32_t batch,
              const void *x, const uint32_t *tokens, uint32_t *draft, void *logits, void *ws,
-             hipStream_t s)
+             hipStream_t s, uint32_t *row_ctr = nullptr)
 {
     const WsLayout L = ws_layout(w->hidden, batch);
     if (batch > 1) {
@@ -243,6 +245,7 @@ int run_head(const mtp_weights *w, bool fp8, const uint8_t *q, const float *scal
     a.logits = static_cast<uint16_t *>(logits);
     a.partials = reinterpret_cast<Partial *>(ws_at(ws, L.part_off));
     a.draft = draft;
+    a.row_ctr = row_ctr;
     if (launch_head(a, fp8, batch, s) != hipSuccess)
         return MTP_ERR_HIP;
     return MTP_OK;
@@ -259,9 +262,12 @@ int run_sweep(const mtp_weights *w, bool fp8, const uint8_t *q, const float *sca
         MTP_TRY(run_front_batched(w, batch, tokens, hidden, x, xn, ws, s));
         return run_head_batched(w, fp8, q, scale, batch, xn, tokens, draft, logits, ws, s);
     }
-    if (launch_eh_proj(front_args(w, tokens, hidden, x), batch, s) != hipSuccess)
+    uint32_t *ctr = reinterpret_cast<uint32_t *>(ws_at(ws, L.ctr_off));
+    RowGemvArgs f = front_args(w, tokens, hidden, x);
+    f.zero_ctr = ctr;  // the head's row counters, cleared for it
+    if (launch_eh_proj(f, batch, s) != hipSuccess)
         return MTP_ERR_HIP;
-    return run_head(w, fp8, q, scale, batch, x, tokens, draft, logits, ws, s);
+    return run_head(w, fp8, q, scale, batch, x, tokens, draft, logits, ws, s, ctr);
 }
 
 int run_draft(const mtp_weights *w, bool fp8, const uint8_t *q, const float *scale,

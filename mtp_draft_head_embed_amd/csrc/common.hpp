@@ -34,12 +34,15 @@ inline size_t align256(size_t n) { return (n + 255) & ~size_t(255); }
 // channels and their atomics do not queue behind one another).
 constexpr int kTilePools = 8;
 constexpr int kCtrStride = 4096;
+// The single-sequence head deals its last passes of rows from kRowPools
+// counters in the same slot (each taken far more often than a tile).
+constexpr int kRowPools = 64;
 
 struct WsLayout {
     size_t x_off, x_bytes;
     size_t part_off, part_bytes;
     size_t concat_off, xn_off, p_off;
-    size_t ctr_off;  // the batched head's tile counters, kTilePools of them kCtrStride bytes apart
+    size_t ctr_off;  // the heads' counters, kCtrStride bytes apart (kTilePools or kRowPools of them)
     size_t total;
 };
 
@@ -64,7 +67,7 @@ inline WsLayout ws_layout(int hidden, int batch)
         L.concat_off = L.xn_off = L.p_off = 0;
     }
     L.ctr_off = L.total;
-    L.total += size_t(kTilePools) * kCtrStride;
+    L.total += size_t(kRowPools > kTilePools ? kRowPools : kTilePools) * kCtrStride;
     return L;
 }
 

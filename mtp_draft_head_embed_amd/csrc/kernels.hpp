@@ -32,6 +32,13 @@ struct RowGemvArgs {
     uint16_t *logits;     // EPI_ARGMAX: [B][N] BF16 or null
     Partial *partials;    // EPI_ARGMAX: [B][kMaxHeadBlocks]
     uint32_t *draft;      // EPI_ARGMAX: [B] argmax, or MTP_DRAFT_INVALID
+    // EPI_ARGMAX, one sequence: kRowPools counters kCtrStride bytes apart, zero
+    // at launch, that the last passes of rows are dealt from; null: every row
+    // dealt round-robin
+    uint32_t *row_ctr;
+    // PRO_FRONT: when not null, the kRowPools counters of the head launched
+    // next, set to zero
+    uint32_t *zero_ctr;
 };
 
 // Batched (B >= 2) GEMM on MFMA: Y[b][n] = sum_k A[b][k] W[n][k].

@@ -172,12 +172,35 @@ __global__ __launch_bounds__(BS) void row_gemv_kernel(RowGemvArgs a)
         }
     };
     auto load_group = [&](int r0, int c0) { load_into(wv, r0, c0); };
+    // The single-sequence head's last three passes on demand (row_ctr set):
+    // the waves do not stream equally fast (its loops ended up to 9 us apart
+    // with fixed shares).  Pool p is the waves of workgroups w with
+    // (w / 8) mod npool = p, one workgroup per XCD at 512 workgroups.  A take
+    // is an atomic every lane issues, lane 0's inside the counters' range,
+    // the others touching no memory.
+    // One row per pass only: with the FP8 head's two (units of two rows in the
+    // tail) the B = 1 FP8 sweep took 174 us against 165 us with fixed shares.
+    const bool dyn = EPI == EPI_ARGMAX && RPI == 1 && a.row_ctr && gridDim.y == 1 &&
+                     a.contig_rows == 0 && nchunks <= U && N / r_outer >= 5;
+    const int PS = dyn ? N / r_outer - 3 : 0x7FFFFFFF, RS = dyn ? PS * r_outer : 0;
+    const int npool = max(1, min(kRowPools, int(gridDim.x) / 8));
+    const int pool = (int(blockIdx.x) / 8) % npool;
+    const __amdgpu_buffer_rsrc_t ctr_rs = __builtin_amdgcn_make_buffer_rsrc(
+        a.row_ctr, 0, dyn ? kRowPools * kCtrStride : 0, 0x00020000);
+    auto take = [&]() {
+        return uint32_t(__builtin_amdgcn_raw_ptr_buffer_atomic_add_i32(
+            1, ctr_rs, lane == 0 ? pool * kCtrStride : int(0x80000000u), 0, 0));
+    };
+    uint32_t gt0 = 0, gt1 = 0;
     // ---- prologue: the BF16 activation vector act[0..K) in LDS -------------
     // The first weight group does not depend on the activation, so its loads
     // are issued before the norm completes.  In the front the norm's loads go
     // first: completion is counted in issue order, so the norm can finish
     // while the weights are still arriving.
     if constexpr (PRO == PRO_FRONT) {
+        // the counters of the head launched next start at zero
+        if (a.zero_ctr && blockIdx.x == 0 && b == 0 && tid < kRowPools)
+            a.zero_ctr[tid * (kCtrStride / 4)] = 0u;
         // K = 2H: [enorm(embed[token]) | hnorm(hidden[b])]
         const int H = K / 2;
         const uint32_t tok = a.tokens[b];
@@ -189,7 +212,12 @@ __global__ __launch_bounds__(BS) void row_gemv_kernel(RowGemvArgs a)
         __builtin_amdgcn_sched_barrier(0);  // keep the weight loads ahead of the norm
         dual_norm_store(nv, H, a.eps, act, act + H, red);
     } else {
-        // K = H: shared_head.norm(x[b]), the first weight group in flight
+        // K = H: shared_head.norm(x[b]), the first weight group in flight (the
+        // tail's first two counts before it: they come back under the norm)
+        if (dyn) {
+            gt0 = take();
+            gt1 = take();
+        }
         load_group(r_begin, 0);
         single_norm(a.xin + size_t(b) * K, a.norm_w, K, a.eps, act, red);
     }
@@ -288,8 +316,13 @@ __global__ __launch_bounds__(BS) void row_gemv_kernel(RowGemvArgs a)
                 consume(wb, q + 1);
         }
     } else {
+        // Every pass but the last three deals rows round-robin; with row_ctr
+        // (one sequence, the eh_proj launch before this one having cleared the
+        // counters) the rows from RS on go in units of RPI consecutive rows
+        // from the wave's pool instead (the tail below).
         bool have_group = true;
-        for (int r0 = r_begin; r0 < r_end; r0 += r_outer) {
+        int pass = 0;
+        for (int r0 = r_begin; r0 < r_end && pass < PS; r0 += r_outer, ++pass) {
             for (int c0 = 0; c0 < nchunks; c0 += U) {
                 if (!have_group)
                     load_group(r0, c0);
@@ -297,6 +330,34 @@ __global__ __launch_bounds__(BS) void row_gemv_kernel(RowGemvArgs a)
                 mac_group(wv, c0);
             }
             finish_rows(r0);
+        }
+        if (dyn) {
+            // Tail: unit g of the wave's pool p is rows RS + (p + npool g) RPI ..;
+            // the wave takes its next unit when it starts one, so a count is
+            // two units ahead of its use (the first two were taken in the
+            // prologue), and the wait for a unit's loads already covers the
+            // count taken before them.  Counts increase: the first unit past
+            // the last row ends the loop.
+            r_inner = 1;
+            auto unit_row = [&](uint32_t g) {
+                return RS + (pool + npool * int(__builtin_amdgcn_readfirstlane(g))) * RPI;
+            };
+            int r0 = unit_row(gt0);
+#pragma unroll 1
+            while (r0 < N) {
+                load_group(r0, 0);
+                gt0 = take();
+                mac_group(wv, 0);
+                finish_rows(r0);
+                r0 = unit_row(gt1);
+                if (r0 >= N)
+                    break;
+                load_group(r0, 0);
+                gt1 = take();
+                mac_group(wv, 0);
+                finish_rows(r0);
+                r0 = unit_row(gt0);
+            }
         }
     }
 
