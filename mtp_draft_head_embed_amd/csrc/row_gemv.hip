@@ -178,8 +178,9 @@ __global__ __launch_bounds__(BS) void row_gemv_kernel(RowGemvArgs a)
     // (w / 8) mod npool = p, one workgroup per XCD at 512 workgroups.  A take
     // is an atomic every lane issues, lane 0's inside the counters' range,
     // the others touching no memory.
-    // One row per pass only: with the FP8 head's two (units of two rows in the
-    // tail) the B = 1 FP8 sweep took 174 us against 165 us with fixed shares.
+    // One row per pass only (RPI is a template argument, so the FP8 head, two
+    // rows per pass, holds no tail code): compiled into the FP8 head the tail
+    // made it 8 us slower (139 -> 147 us) even in calls that never take it.
     const bool dyn = EPI == EPI_ARGMAX && RPI == 1 && a.row_ctr && gridDim.y == 1 &&
                      a.contig_rows == 0 && nchunks <= U && N / r_outer >= 5;
     const int PS = dyn ? N / r_outer - 3 : 0x7FFFFFFF, RS = dyn ? PS * r_outer : 0;
