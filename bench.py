@@ -157,7 +157,7 @@ def cpu_baseline_leg(args, cfg, wts, tokens, hidden) -> dict:
     hc = oracle.host_cores()
     detail = {"cpu": cpu_info(), "host_cores": hc, "threads": nthreads,
               "thread_rule": f"min(os.cpu_count(), affinity, cgroup quota, {oracle.THREAD_CAP}): "
-                             f"a GPU box grants one process about {oracle.THREAD_CAP} host cores"}
+                             f"a one-GPU host grants a process about {oracle.THREAD_CAP} host cores"}
     # the FP8 copy of the bench weights (timed: the quantiser on the host)
     tq = time.perf_counter()
     ref8 = oracle.quantize_fp8(wts["lm_head"], nthreads=nthreads)
@@ -217,7 +217,7 @@ def main():
     args = parse()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the sweep has no "
-              "multi-GPU path in this build.", file=sys.stderr)
+              "multi-GPU path (it runs the whole vocabulary on one GPU).", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np

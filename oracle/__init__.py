@@ -108,7 +108,7 @@ def host_cores() -> dict:
     return info
 
 
-# A GPU machine grants one process about 16 host cores whatever the machine has.
+# A one-GPU host grants a process about 16 host cores, whatever the machine has.
 THREAD_CAP = 16
 
 
