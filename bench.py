@@ -376,33 +376,69 @@ def main():
         print(f"[bench] {name}: {res[name]}", file=sys.stderr, flush=True)
 
     # The per-GPU kernel of a vocabulary-sharded head (the pages' TP sweep):
-    # the head over the first V/G rows, what one of G GPUs would sweep before
-    # the cross-GPU pick.  Only the kernel is timed here; the exchange of the
+    # the head over V/G rows, what one of G GPUs would sweep before the
+    # cross-GPU pick.  Only the kernel is timed here; the exchange of the
     # per-shard (max, index) is not built.
     shards = None
     if not args.no_shards:
         shards = {}
         t = dw.tensors
+
+        def shard_tables(G):
+            # Consecutive calls read different row ranges of the tables (up to
+            # three shards of V/G rows): one shard read over and over would
+            # partly stay in the 256 MB last-level cache, which a sharded
+            # sweep, reading its rows once per draft, does not get.
+            Vs = V // G
+            tabs = []
+            for i in range(min(G, 3)):
+                r = slice(i * Vs, (i + 1) * Vs)
+                tabs.append((mtp.mtp_weights(t["embed"][r], t["enorm_w"], t["hnorm_w"],
+                                             t["head_norm_w"], t["eh_proj"], t["lm_head"][r],
+                                             float(wts["rms_eps"])), q[r], s[r]))
+            return [a for a, _, _ in tabs], [b for _, b, _ in tabs], [c for _, _, c in tabs]
+
+        # A plain streaming read of the same bytes, rotated the same way (best
+        # of one and two workgroups per CU): the practical floor at this size,
+        # launch and drain included, against which the head's fixed costs show.
+        probe_out = torch.zeros(1, dtype=torch.int32, device=dev)
+        probe_cache = {}
+
+        def read_floor_us(G, fp8):
+            if (G, fp8) not in probe_cache:
+                Vs = V // G
+                bufs = [(q if fp8 else t["lm_head"])[i * Vs:(i + 1) * Vs] for i in range(min(G, 3))]
+                best = None
+                for per_cu in (1, 2):
+                    def rd(c=[0]):
+                        mtp.mtp_probe_stream_read(bufs[c[0] % len(bufs)], probe_out, per_cu, stream)
+                        c[0] += 1
+                    g_s, _ = timed(rd, args.steps, args.warmup)
+                    us = g_s / args.steps * 1e6
+                    best = us if best is None else min(best, us)
+                probe_cache[(G, fp8)] = round(best, 2)
+            return probe_cache[(G, fp8)]
         for G in (2, 4, 8):
             Vs = V // G
-            # the first Vs rows of each [V][H] table (the head reads no embedding)
-            sw = mtp.mtp_weights(t["embed"][:Vs], t["enorm_w"], t["hnorm_w"], t["head_norm_w"],
-                                 t["eh_proj"], t["lm_head"][:Vs], float(wts["rms_eps"]))
+            sws_, qs_, ss_ = shard_tables(G)
             slg = torch.empty((B, Vs), dtype=torch.bfloat16, device=dev)
             sws = mtp.new_workspace(H, Vs, B)
-            ent = {"rows": Vs}
+            ent = {"rows": Vs, "row_ranges": len(sws_)}
             for name, fp8 in (("bf16", False), ("fp8", True)):
-                def shead():
+                def shead(c=[0]):
+                    i = c[0] % len(sws_)
+                    c[0] += 1
                     if fp8:
-                        mtp.mtp_head_fp8w(sw, q[:Vs], s[:Vs], B, x, draft, slg, sws, stream)
+                        mtp.mtp_head_fp8w(sws_[i], qs_[i], ss_[i], B, x, draft, slg, sws, stream)
                     else:
-                        mtp.mtp_head_bf16(sw, B, x, draft, slg, sws, stream)
+                        mtp.mtp_head_bf16(sws_[i], B, x, draft, slg, sws, stream)
                 g_s, _ = timed(shead, args.steps, args.warmup)
                 per = g_s / args.steps
                 ent[name] = {"head_us": round(per * 1e6, 2),
                              "GBps": round(head_bytes(H, Vs, B, fp8) / per / 1e9, 1),
                              "frac_of_peak": round(head_bytes(H, Vs, B, fp8) / per / 1e9
-                                                   / HBM_PEAK_GBPS, 4)}
+                                                   / HBM_PEAK_GBPS, 4),
+                             "weight_read_floor_us": read_floor_us(G, fp8)}
             shards[f"G{G}"] = ent
         if args.config == "large":
             # the same shard shapes for the batched configuration's 16 sequences
@@ -412,23 +448,25 @@ def main():
             db = torch.empty(16, dtype=torch.int32, device=dev)
             for G in (1, 2, 4, 8):
                 Vs = V // G
-                sw = mtp.mtp_weights(t["embed"][:Vs], t["enorm_w"], t["hnorm_w"], t["head_norm_w"],
-                                     t["eh_proj"], t["lm_head"][:Vs], float(wts["rms_eps"]))
+                sws_, qs_, ss_ = shard_tables(G)
                 slg = torch.empty((16, Vs), dtype=torch.bfloat16, device=dev)
                 sws = mtp.new_workspace(H, Vs, 16)
-                ent = {"rows": Vs, "batch": 16}
+                ent = {"rows": Vs, "batch": 16, "row_ranges": len(sws_)}
                 for name, fp8 in (("bf16", False), ("fp8", True)):
-                    def shead():
+                    def shead(c=[0]):
+                        i = c[0] % len(sws_)
+                        c[0] += 1
                         if fp8:
-                            mtp.mtp_head_fp8w(sw, q[:Vs], s[:Vs], 16, xb, db, slg, sws, stream)
+                            mtp.mtp_head_fp8w(sws_[i], qs_[i], ss_[i], 16, xb, db, slg, sws, stream)
                         else:
-                            mtp.mtp_head_bf16(sw, 16, xb, db, slg, sws, stream)
+                            mtp.mtp_head_bf16(sws_[i], 16, xb, db, slg, sws, stream)
                     g_s, _ = timed(shead, args.steps, args.warmup)
                     per = g_s / args.steps
                     ent[name] = {"head_us": round(per * 1e6, 2),
                                  "GBps": round(head_bytes(H, Vs, 16, fp8) / per / 1e9, 1),
                                  "frac_of_peak": round(head_bytes(H, Vs, 16, fp8) / per / 1e9
-                                                       / HBM_PEAK_GBPS, 4)}
+                                                       / HBM_PEAK_GBPS, 4),
+                                 "weight_read_floor_us": read_floor_us(G, fp8)}
                 shards[f"B16_G{G}"] = ent
         print(f"[bench] vocab shards: {shards}", file=sys.stderr, flush=True)
 

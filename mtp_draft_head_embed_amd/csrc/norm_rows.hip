@@ -25,6 +25,9 @@ __global__ __launch_bounds__(256) void front_concat_kernel(FrontArgs a)
               dst + H, red);
 }
 
+// UB: partial sums loaded per batch (4 when S <= 4, as for the fused front's
+// four K splits, so no split is read twice; else 8)
+template <int UB>
 __global__ __launch_bounds__(512) void sum_norm_kernel(SumNormArgs a)
 {
     __shared__ float red[32];
@@ -38,9 +41,9 @@ __global__ __launch_bounds__(512) void sum_norm_kernel(SumNormArgs a)
         return;
     }
     // x = BF16(sum_s P[s][b]) in split order.  The partial sums are loaded
-    // eight splits at a time for both pieces (a split past S re-reads the
-    // last one and is not added), all issued before the first add, so a batch
-    // of splits costs one memory latency rather than one per split.
+    // UB splits at a time for both pieces (a split past S re-reads the last
+    // one and is not added), all issued before the first add, so a batch of
+    // splits costs one memory latency rather than one per split.
     uint4 v[2], wv[2];
     float acc[2][8];
     bool in[2];
@@ -55,14 +58,14 @@ __global__ __launch_bounds__(512) void sum_norm_kernel(SumNormArgs a)
         for (int e = 0; e < 8; ++e)
             acc[i][e] = 0.f;
     }
-    for (int sp0 = 0; sp0 < a.S; sp0 += 8) {
-        float4 p[2][8][2];
+    for (int sp0 = 0; sp0 < a.S; sp0 += UB) {
+        float4 p[2][UB][2];
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
             // a piece past H reads piece 0 of the row (never added)
             const int j = in[i] ? (i * blockDim.x + tid) * 8 : 0;
 #pragma unroll
-            for (int u = 0; u < 8; ++u) {
+            for (int u = 0; u < UB; ++u) {
                 const int sp = min(sp0 + u, a.S - 1);
                 const float *src = a.P + (size_t(sp) * a.B + b) * H + j;
                 p[i][u][0] = *reinterpret_cast<const float4 *>(src);
@@ -72,7 +75,7 @@ __global__ __launch_bounds__(512) void sum_norm_kernel(SumNormArgs a)
 #pragma unroll
         for (int i = 0; i < 2; ++i)
 #pragma unroll
-            for (int u = 0; u < 8; ++u)
+            for (int u = 0; u < UB; ++u)
                 if (sp0 + u < a.S) {
                     acc[i][0] += p[i][u][0].x; acc[i][1] += p[i][u][0].y;
                     acc[i][2] += p[i][u][0].z; acc[i][3] += p[i][u][0].w;
@@ -140,7 +143,10 @@ hipError_t launch_front_concat(const FrontArgs &a, int batch, hipStream_t s)
 hipError_t launch_sum_norm(const SumNormArgs &a, int batch, hipStream_t s)
 {
     // 512 threads x 2 pieces of 8 cover H <= 8192
-    hipLaunchKernelGGL(sum_norm_kernel, dim3(batch), dim3(512), 0, s, a);
+    if (a.S <= 4)
+        hipLaunchKernelGGL(sum_norm_kernel<4>, dim3(batch), dim3(512), 0, s, a);
+    else
+        hipLaunchKernelGGL(sum_norm_kernel<8>, dim3(batch), dim3(512), 0, s, a);
     return hipGetLastError();
 }
 
