@@ -3,7 +3,7 @@ variant the launcher picks, against the FP64 oracle.
 
 The batched head streams lm_head once for all B sequences; which kernel runs
 depends on B and H only:
-  * 2 <= B <= 16 at H <= 6144: the tile kernel (head_tile.hip), one 16-row
+  * 2 <= B <= 16 at H <= 6144: the tile kernel (tile_gemm.hip), one 16-row
     tile per workgroup with K split over its 8 waves; the wave's slice of each
     row is 2, 4 or 6 segments of 128 bytes per chunk, one chunk (FP8, and BF16
     to H = 3072) or two (BF16 above);
