@@ -304,9 +304,9 @@ def main():
     # 256 MB last-level cache), used in turn by the cold-front sweeps and the
     # context rows, so those calls stream eh_proj from HBM
     t = dw.tensors
+    ehc = [t["eh_proj"]] + [t["eh_proj"].clone() for _ in range(2)]
     cw = [dw.w] + [mtp.mtp_weights(t["embed"], t["enorm_w"], t["hnorm_w"], t["head_norm_w"],
-                                   t["eh_proj"].clone(), t["lm_head"], float(wts["rms_eps"]))
-                   for _ in range(2)]
+                                   e, t["lm_head"], float(wts["rms_eps"])) for e in ehc[1:]]
 
     def spread(fn, blocks=20, per=10):
         """Per-call µs from HIP events around blocks of back-to-back calls:
@@ -652,6 +652,24 @@ def main():
                    "buffer": f"the BF16 lm_head, {nb} bytes",
                    "lm_head_bf16_frac_of_ceiling": round(res["bf16"]["lm_head_GBps"] / best[0], 4),
                    "lm_head_fp8_frac_of_ceiling": round(res["fp8"]["lm_head_GBps"] / best[0], 4)}
+        if B == 1:
+            # The sweep against plain reads of its two weight matrices: the same
+            # probe over eh_proj (the three copies in turn, as the cold-front
+            # sweeps read them) plus the lm_head read above.
+            eh_us = None
+            for per_cu in (1, 2):
+                def rd(c=[0]):
+                    mtp.mtp_probe_stream_read(ehc[c[0] % len(ehc)], pout, per_cu, stream)
+                    c[0] += 1
+                g_s, _ = timed(rd, max(20, args.steps // 4), 5)
+                us = g_s / max(20, args.steps // 4) * 1e6
+                eh_us = us if eh_us is None else min(eh_us, us)
+            lm_us = nb / best[0] / 1e3
+            sweep_us = res["bf16"]["ms_per_step"] * 1e3
+            ceiling["bf16_sweep_vs_plain_reads"] = {
+                "eh_proj_read_us": round(eh_us, 2), "lm_head_read_us": round(lm_us, 2),
+                "sum_us": round(eh_us + lm_us, 2), "sweep_us": round(sweep_us, 2),
+                "sweep_over_sum": round(sweep_us / (eh_us + lm_us), 4)}
         print(f"[bench] streaming-read ceiling: {ceiling}", file=sys.stderr, flush=True)
 
     main_path = "bf16"
