@@ -9,9 +9,10 @@
 // both operands K-contiguous, HBM-bound for a few hundred rows and bound by
 // the matrix cores beyond.  One kernel, three tile shapes:
 //   * 256 x 256 or 256 x 192 output tile per 16-wave workgroup (one per CU)
-//     for many rows (whichever fills the CUs in whole rounds), 128 x 128 per
-//     8-wave workgroup up to 128 rows; every wave owns a 64 x 64, 64 x 48 or
-//     64 x 32 block of v_mfma_f32_16x16x32_bf16 accumulators;
+//     for many rows (whichever fills the CUs in whole rounds; the 192-wide
+//     tile on 8 waves when its grid is whole rounds), 128 x 128 per 8-wave
+//     workgroup up to 128 rows; every wave owns a 64 x 64, 64 x 96, 64 x 48
+//     or 64 x 32 block of v_mfma_f32_16x16x32_bf16 accumulators;
 //   * K in steps of 64 columns (128-byte staged rows, 8 rows per load
 //     instruction) through LDS stages, each its own LDS object; the operands
 //     go from HBM straight into LDS (buffer loads with the LDS flag: no
@@ -94,17 +95,18 @@ __global__ __launch_bounds__(WM *WN * 64) void ctx_gemm_kernel(const uint16_t *_
     constexpr int NW = WM * WN;
     constexpr int FM = BM / WM / 16, FN = BN / WN / 16;
     static_assert(FM == 4, "the staged waits below assume four A fragments per wave");
-    static_assert(FN >= 2 && FN <= 4, "two to four W fragments per wave");
+    static_assert((FN >= 2 && FN <= 4) || FN == 6, "two to four, or six, W fragments per wave");
     // A load instruction stages RPL rows (16 of 64 bytes or 8 of 128).  The A
-    // rows go to the waves in equal contiguous shares; so do the W rows when
-    // they divide evenly, else W row group q (16 rows) goes to wave q, and the
+    // rows go to the waves in equal contiguous shares of whole load
+    // instructions; so do the W rows when they divide so (192 rows over 8
+    // waves: 24 each), else W row group q (16 rows) goes to wave q, and the
     // waves past the last group stage nothing real: their load reads past the
     // resource (zeros) into a slot of 16 staged rows past the stage, so every
     // wave issues the same number of loads per step and the vmcnt waits below
     // hold for all of them.
     constexpr int RA = BM / NW;
-    static_assert(RA % 16 == 0 && BN % 16 == 0, "waves stage whole 16-row groups");
-    constexpr bool WSPLIT = (BN / NW) % 16 == 0;
+    static_assert(RA % RPL == 0 && BN % 16 == 0, "waves stage whole load instructions");
+    constexpr bool WSPLIT = (BN / NW) % RPL == 0;
     static_assert(WSPLIT || BN / 16 <= NW, "uneven W staging takes one group per wave");
     constexpr int RW = WSPLIT ? BN / NW : 16;
     constexpr int IA = RA / RPL, IW = RW / RPL;
@@ -215,7 +217,11 @@ __global__ __launch_bounds__(WM *WN * 64) void ctx_gemm_kernel(const uint16_t *_
         for (int i = 0; i < FM; ++i)
             asm volatile("ds_read_b128 %0, %1" : "=v"(a[i]) : "v"(base + ao[i]));
         // W and A row i are in once at most 3 - i reads are outstanding
-        if constexpr (FN == 4)
+        if constexpr (FN == 6)
+            asm volatile("s_waitcnt lgkmcnt(3)"
+                         : "+v"(a[0]), "+v"(w[0]), "+v"(w[1]), "+v"(w[2]), "+v"(w[3]), "+v"(w[4]),
+                           "+v"(w[5]));
+        else if constexpr (FN == 4)
             asm volatile("s_waitcnt lgkmcnt(3)"
                          : "+v"(a[0]), "+v"(w[0]), "+v"(w[1]), "+v"(w[2]), "+v"(w[3]));
         else if constexpr (FN == 3)
@@ -245,7 +251,11 @@ __global__ __launch_bounds__(WM *WN * 64) void ctx_gemm_kernel(const uint16_t *_
 #pragma unroll
         for (int i = 0; i < FM; ++i)
             asm volatile("ds_read_b128 %0, %1" : "=v"(a[i]) : "v"(base + aoff[0][i]));
-        if constexpr (FN == 4)
+        if constexpr (FN == 6)
+            asm volatile("s_waitcnt lgkmcnt(3)"
+                         : "+v"(a[0]), "+v"(w[0]), "+v"(w[1]), "+v"(w[2]), "+v"(w[3]), "+v"(w[4]),
+                           "+v"(w[5]));
+        else if constexpr (FN == 4)
             asm volatile("s_waitcnt lgkmcnt(3)"
                          : "+v"(a[0]), "+v"(w[0]), "+v"(w[1]), "+v"(w[2]), "+v"(w[3]));
         else if constexpr (FN == 3)
@@ -270,7 +280,11 @@ __global__ __launch_bounds__(WM *WN * 64) void ctx_gemm_kernel(const uint16_t *_
 #pragma unroll
         for (int j = 0; j < FN; ++j)
             asm volatile("ds_read_b128 %0, %1" : "=v"(w[j]) : "v"(base + woff[1][j]));
-        if constexpr (FN == 4)
+        if constexpr (FN == 6)
+            asm volatile("s_waitcnt lgkmcnt(0)"
+                         : "+v"(a[0]), "+v"(a[1]), "+v"(a[2]), "+v"(a[3]), "+v"(w[0]), "+v"(w[1]),
+                           "+v"(w[2]), "+v"(w[3]), "+v"(w[4]), "+v"(w[5]));
+        else if constexpr (FN == 4)
             asm volatile("s_waitcnt lgkmcnt(0)"
                          : "+v"(a[0]), "+v"(a[1]), "+v"(a[2]), "+v"(a[3]), "+v"(w[0]), "+v"(w[1]),
                            "+v"(w[2]), "+v"(w[3]));
@@ -418,8 +432,17 @@ hipError_t launch_ctx_gemm(const uint16_t *A, const uint16_t *W, uint16_t *C, fl
     switch (sp.tile) {
     case kCtxTile256x256:
         return launch_ctx_tile<256, 256, 4, 4, 64, 2>(A, W, C, P, M, N, K, sp, s);
-    case kCtxTile256x192:
+    case kCtxTile256x192: {
+        // 8 waves of 64 x 96 when the grid fills whole rounds of one
+        // workgroup per CU (a third fewer fragment reads from LDS per flop
+        // than 16 waves of 64 x 48: T = 4096 3% faster, T = 1024 and 2048
+        // level); 16 waves when the last round is part-filled (T = 3072: 2%
+        // faster than 8)
+        const long wgs = long((N + 191) / 192) * long((M + 255) / 256) * sp.S;
+        if (wgs % device_cu_count() == 0)
+            return launch_ctx_tile<256, 192, 4, 2, 64, 2>(A, W, C, P, M, N, K, sp, s);
         return launch_ctx_tile<256, 192, 4, 4, 64, 2>(A, W, C, P, M, N, K, sp, s);
+    }
     default:
         return launch_ctx_tile<128, 128, 2, 4, 64>(A, W, C, P, M, N, K, sp, s);
     }

@@ -77,6 +77,14 @@ def test_context_rows_large_big_tile():
                                        513, 598, 599])
 
 
+@pytest.mark.slow
+def test_context_rows_large_whole_rounds():
+    """H = 6144, T = 1024: the 256 x 192 tile on 8 waves (K split two ways, 256
+    workgroups, one whole round); sampled rows on both sides of every row-tile
+    edge, checked against the oracle."""
+    _run(6144, 20000, 1024, 103, sample=[0, 1, 255, 256, 257, 511, 512, 767, 768, 1022, 1023])
+
+
 def test_context_rows_max_rows():
     """T = 65 536 (the maximum) at H = 16: 256 row tiles of the large tile."""
     _run(16, 100, 65536, 99)
