@@ -363,6 +363,44 @@ def test_neartie_bf16_and_fp8():
          f"FP8 exact-tie sequences: {exact_fp8}/{cfg.batch}")
 
 
+def test_concurrent_streams():
+    """Calls on two streams at once, each with its own workspace and buffers
+    (a B = 1 BF16 sweep, whose head deals its last rows from counters in its
+    workspace, beside a B = 3 FP8 sweep on the tile kernels), issued in turn
+    without synchronising: each stream's outputs equal the same call made
+    alone, bit for bit.  The library keeps no state between calls, so
+    overlapping calls share nothing but the weights they read."""
+    import mtp_draft_head_embed_amd as mtp
+    H, V = 1024, 20000
+    _say(f"\n[streams] H={H} V={V}")
+    cfg = synth.custom(H, V, 4, 71)
+    wts = synth.make_weights(cfg)
+    dw = harness.upload(wts)
+    q, s = harness.quantize_dev(dw)
+    tokens, hidden = synth.make_inputs(cfg)
+    runs = []
+    for B, fp8, lo in ((1, False, 0), (3, True, 1)):
+        tok, hid = tokens[lo:lo + B], hidden[lo:lo + B]
+        tk = torch.from_numpy(tok.astype(np.uint32).view(np.int32)).cuda()
+        hd = harness.to_dev_bf16(hid)
+        dr = torch.empty(B, dtype=torch.int32, device="cuda")
+        lg = torch.full((B, V), float("nan"), dtype=torch.bfloat16, device="cuda")
+        ws = mtp.new_workspace(H, V, B)
+        runs.append((B, fp8, tok, hid, tk, hd, dr, lg, ws, torch.cuda.Stream()))
+    torch.cuda.synchronize()
+    for _ in range(8):
+        for B, fp8, _t, _h, tk, hd, dr, lg, ws, st in runs:
+            if fp8:
+                mtp.mtp_draft_fp8w(dw.w, q, s, B, tk, hd, dr, lg, ws, st)
+            else:
+                mtp.mtp_draft_bf16(dw.w, B, tk, hd, dr, lg, ws, st)
+    torch.cuda.synchronize()
+    for B, fp8, tok, hid, tk, hd, dr, lg, ws, st in runs:
+        d_e, l_e = harness.run_draft(dw, tok, hid, fp8=(q, s) if fp8 else None)
+        assert np.array_equal(dr.cpu().numpy().view(np.uint32), d_e), (B, fp8)
+        assert np.array_equal(harness.bf16_bits(lg), l_e), (B, fp8)
+
+
 @pytest.mark.parametrize("B,H", [(1, 1024), (3, 1024), (1, 6144)])
 def test_graph_capture_replay(B, H):
     """A captured draft call replays correctly: new inputs copied into the
