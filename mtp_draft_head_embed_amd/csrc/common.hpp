@@ -21,6 +21,15 @@ constexpr int kWave = 64;
 //   P        FP32 [S][B][H]     batched path: eh_proj split-K partial sums
 // ---------------------------------------------------------------------------
 constexpr int kMaxHeadBlocks = 4096;
+// Per sequence, the partial slots from kLogitSinkFirst on are never a
+// workgroup's (the row kernels' grids stay below it): the single-sequence head
+// stores each rounded logit into kLogitSinkSlots 2-byte slots there as it
+// finishes the row (8 KiB, resident in L2), which keeps its rows streaming at
+// full rate; the logits buffer is written from LDS in batches.
+constexpr int kLogitSinkFirst = kMaxHeadBlocks / 2;
+constexpr int kLogitSinkSlots = 4096;
+static_assert(kLogitSinkSlots * 2 <= (kMaxHeadBlocks - kLogitSinkFirst) * 8,
+              "the sink fits in the sequence's spare partial slots");
 
 struct Partial {
     float val;
