@@ -467,6 +467,30 @@ def test_graph_capture_replay(B, H):
 
 
 @pytest.mark.slow
+def test_head_logit_batches():
+    """The single-sequence heads write their logits from LDS 128 rows per wave
+    at a time: at H = 4608 (the same kernel instantiations as H = 6144, one
+    row per pass BF16 and two FP8) and V = 300 000 every wave holds about 146
+    rows, so each writes one batch inside its loop and the rest after it.
+    Every logit of both heads, with and without the logits buffer, against the
+    oracle."""
+    H, V = 4608, 300000
+    _say(f"\n[logit batches] H={H} V={V}")
+    cfg = synth.custom(H, V, 1, 75)
+    wts = synth.make_weights(cfg)
+    tokens, hidden = synth.make_inputs(cfg)
+    dw = harness.upload(wts)
+    d, _, _ = _check_all(cfg, wts, tokens, hidden, dw)
+    d0, _, _ = _check_all(cfg, wts, tokens, hidden, dw, with_logits=False)
+    assert np.array_equal(d, d0)
+    q, s = harness.quantize_dev(dw)
+    ref = oracle.quantize_fp8(wts["lm_head"])
+    d8, _, _ = _check_all(cfg, wts, tokens, hidden, dw, (q, s), ref)
+    d80, _, _ = _check_all(cfg, wts, tokens, hidden, dw, (q, s), ref, with_logits=False)
+    assert np.array_equal(d8, d80)
+
+
+@pytest.mark.slow
 @pytest.mark.parametrize("B", [1, 2])
 def test_max_vocab(B):
     """The largest vocabulary the ABI accepts (2^24 rows) at the smallest
